@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of the int4 routed-expert MoE layer on one MI355X.
+
+A step is one whole layer forward (route -> permute -> shared expert ->
+grouped gate/up + SwiGLU -> grouped down -> combine, plus the latent
+wrapper / exact quantiser where the workload has them) over one batch of
+seeded synthetic tokens already resident in HBM.  Default workload: the
+Kimi-K2.5-shaped decode layer (T=64, hidden 7168, 384 experts, top-8,
+intermediate 2048, one bf16 shared expert).
+
+Prints ONE JSON line: tokens/s over exactly --steps timed steps (after
+--warmup untimed ones), the dominant kernel's roofline fraction measured with
+HIP events on the launch stream, and the CPU oracle timed on a bounded token
+sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_F16_PEAK_TFS = 2500.0  # dense fp16/bf16 matrix cores
+INT8_PEAK_TOPS = 5000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
+                    help="1 tiny, 2 K2.5 decode (default), 3 K2.5 prefill, 4 exact-mode Zipf, 5 K3 latent")
+    ap.add_argument("--kernel-steps", type=int, default=10, help="forwards timed per kernel with events")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_work(cfg, counts, shared_I):
+    """Bytes each call must move and flops it must do (weights of routed experts only)."""
+    T, E, k, H, I = cfg["T"], cfg["E"], cfg["k"], cfg["H"], cfg["I"]
+    K = cfg["L"] or H
+    S = T * k
+    active = int((counts > 0).sum())
+    exact = cfg["mode"] == "exact"
+    gu_w = 2 * (I * K // 2 + I * (K // 32) * 2)   # gate+up packed + scales, per expert
+    d_w = K * I // 2 + K * (I // 32) * 2           # down
+    act_in = T * K * (1 if exact else 2) + (T * (K // 32) * 4 if exact else 0)
+    h_bytes = S * I * (1 if exact else 2) + (S * (I // 32) * 4 if exact else 0)
+    y_bytes = S * K * (4 if exact else 2)
+    work = {
+        "moe_route": (E * H * 2 + T * H * 2 + T * k * 8, 2 * T * E * H),
+        "moe_permute": (T * k * 4 * 3 + E * 8, 0),
+        "moe_int4_grouped_swiglu": (active * gu_w + act_in + h_bytes, 2 * S * 2 * K * I),
+        "moe_int4_grouped_down": (active * d_w + h_bytes + y_bytes, 2 * S * I * K),
+        "moe_combine": (y_bytes + T * K * (4 if exact else 2) + (T * H * 2 if shared_I and not cfg["L"] else 0),
+                        2 * S * K),
+    }
+    if exact:
+        work["moe_quant_act_int8"] = (T * K * 2 + act_in, 0)
+    if shared_I:
+        work["shared_gate_up"] = (2 * shared_I * H * 2 + T * H * 2 + T * shared_I * 2, 2 * T * 2 * H * shared_I)
+        work["shared_down"] = (H * shared_I * 2 + T * shared_I * 2 + T * H * 2, 2 * T * shared_I * H)
+    if cfg["L"]:
+        L = cfg["L"]
+        work["latent_down"] = (L * H * 2 + T * H * 2 + T * L * 2, 2 * T * L * H)
+        work["moe_rmsnorm_bf16"] = (2 * T * L * 2 + L * 2, 0)
+        work["latent_up"] = (H * L * 2 + T * L * 2 + 2 * T * H * 2, 2 * T * L * H)
+    layer_bytes = (active * (gu_w + d_w) + E * H * 2 + E * 4 + T * H * 2 + T * H * (4 if exact else 2)
+                   + (3 * shared_I * H * 2 if shared_I else 0)
+                   + (2 * cfg["L"] * H * 2 + cfg["L"] * 2 if cfg["L"] else 0))
+    layer_flops = sum(f for n, (b, f) in work.items() if n != "moe_route")
+    return work, layer_bytes, layer_flops, active
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel, workload_name):
+    """HBM traffic measured with rocprofv3 counters for this kernel and workload, if
+    the record was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_digest(rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from int4_routed_expert_moe_amd import synthetic
+    from int4_routed_expert_moe_amd.layer import MoELayer
+
+    cfg0 = synthetic.CONFIGS[args.workload]
+    bias = None
+    if cfg0.get("zipf"):
+        bias = synthetic.load_bias_file(os.path.join(ROOT, "tests", "golden", "zipf_bias_k25.txt"))
+    t_gen = time.perf_counter()
+    inp = synthetic.make_inputs(args.workload, router_bias=bias)
+    cfg = inp["cfg"]
+    layer = MoELayer.from_numpy(inp, "cuda")
+    x = torch.from_numpy(inp["x"].view(np.int16)).cuda().view(torch.bfloat16)
+    t_gen = time.perf_counter() - t_gen
+    T = cfg["T"]
+
+    for _ in range(args.warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        layer.forward(x)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+
+    # per-call durations from events recorded between the calls, on the launch stream
+    per = {}
+    for _ in range(args.kernel_steps):
+        marks = []
+        layer.forward(x, marks=marks)
+        torch.cuda.synchronize()
+        for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
+            per.setdefault(name, []).append(a.elapsed_time(b))
+    kernel_ms = {n: float(np.mean(v)) for n, v in per.items()}
+
+    ws = layer.workspace(T)
+    counts = ws["counts"].cpu().numpy()
+    work, layer_bytes, layer_flops, active = algorithmic_work(cfg, counts, cfg["shared_I"])
+    dom = max((n for n in kernel_ms if n in work), key=lambda n: kernel_ms[n])
+    b, f = work[dom]
+    dur_s = kernel_ms[dom] / 1e3
+    intensity = f / max(b, 1)
+    if intensity < MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": b / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": f / dur_s / 1e12, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_record(dom, cfg["name"])
+    roof["kernel"] = dom
+    roof["kernel_ms"] = kernel_ms[dom]
+    roof["algorithmic_bytes"] = b
+    roof["algorithmic_flops"] = f
+
+    step_s = ms_per_step / 1e3
+    line = {
+        "metric": "MoE-layer tokens/s at 1 GPU + % of HBM (decode) / MFMA (prefill) roofline",
+        "value": T / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4xf16-mfma" if cfg["mode"] != "exact" else "int4xint8-exact",
+        "data": "synthetic (seeded; random-init weights of the layer's shapes)",
+        "config": {
+            "workload": (f"{cfg['name']}: T={T} hidden={cfg['H']} experts={cfg['E']} top-{cfg['k']} "
+                         f"intermediate={cfg['I']}" + (f" latent={cfg['L']}" if cfg["L"] else "")
+                         + (f" shared={cfg['shared_I']}" if cfg["shared_I"] else "") + f" mode={cfg['mode']}"),
+            "tokens": T,
+            "active_experts": active,
+            "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "layer_roofline": {
+            "bytes": layer_bytes, "flops": layer_flops,
+            "hbm_frac": layer_bytes / step_s / (HBM_PEAK_GBS * 1e9),
+            "mfma_frac": layer_flops / step_s / (MFMA_F16_PEAK_TFS * 1e12),
+        },
+        "kernel_ms": kernel_ms,
+        "wall_s_timed": wall,
+        "setup_s": t_gen,
+    }
+    if cfg["mode"] == "exact":
+        line["layer_roofline"]["int8_frac"] = layer_flops / step_s / (INT8_PEAK_TOPS * 1e12)
+
+    if not args.no_cpu_baseline:
+        import oracle
+        toks_probe = synthetic.token_sample(cfg, min(4, T), salt=1)
+        t0 = time.perf_counter()
+        oracle.layer_tokens(inp, toks_probe)
+        per_tok = (time.perf_counter() - t0) / len(toks_probe)
+        n = int(max(len(toks_probe), min(T, args.cpu_seconds / max(per_tok, 1e-9))))
+        toks = synthetic.token_sample(cfg, n, salt=2)
+        t0 = time.perf_counter()
+        oracle.layer_tokens(inp, toks)
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {
+            "value": len(toks) / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{len(toks)} of {T} tokens of the same workload (routing of the sampled tokens "
+                      f"included), {el:.1f} s",
+        }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,395 @@
+// Dense bf16 pieces around the routed experts: the shared expert (a bf16
+// SwiGLU MLP on the full-width input) and the Kimi-K3 latent down/up
+// projections ("Kimi exact-generator adaptation", "The proposed
+// substitution": shared experts keep ordinary bf16 linear layers; "Kimi-K3
+// latent MoE", Parameters table: weights held [out, in], no bias; "Kimi K2.5
+// donor reference", record "Add an always-active shared expert"), plus the
+// RMSNorm before the latent up-projection (records "RMSNorm mean square",
+// "Normalize by the root mean square", "Apply learned per-feature RMSNorm
+// gains").
+//
+// GEMM C = A W^T with A [M,K], W [N,K] both K-contiguous: the natural operand
+// layout of v_mfma_f32_16x16x32_bf16 (each lane holds 8 consecutive k of one
+// row / one weight row).  A workgroup of 4 waves stages a 16*MB-row A tile in
+// LDS per 128-wide K chunk; each wave streams its own 16*CB weight rows
+// straight from global memory (16 bytes per lane).  Decode-shaped problems
+// (few rows) split K over the grid and write fp32 partials that a second
+// kernel sums in a fixed order (deterministic), then applies the epilogue.
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kDKC = 128;
+constexpr int kDAStride = 136;  // bf16 per LDS row
+
+enum { EPI_LINEAR = 0, EPI_SWIGLU = 1 };
+
+struct DenseArgs {
+    const uint16_t* x;   // [M,K]
+    const uint16_t* w0;  // [N0,K]  (linear: W; swiglu: W_gate)
+    const uint16_t* w1;  // swiglu: W_up [N0,K]
+    const uint16_t* add; // linear: optional [M,N0]
+    uint16_t* y;         // [M,N0]
+    float* part;         // split-K partials [ks][M][Ntot]
+    int M, N0, K;
+    int Ntot;            // N0 (linear) or 2*N0 (swiglu)
+    int tiles_m, n_chunks, ksplit;
+    long n_logical;
+    int per_xcd;
+};
+
+__device__ __forceinline__ uint32_t silu_mul_bits(float g, float u) {
+    const uint32_t gb = f32_to_bf16_bits(g);
+    const uint32_t ub = f32_to_bf16_bits(u);
+    const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
+    return f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
+}
+
+__device__ __forceinline__ uint32_t add_bits(uint32_t yb, uint16_t addv) {
+    return f32_to_bf16_bits(bf16_bits_to_f32(yb) + bf16_bits_to_f32(addv));
+}
+
+// Column layout of a wave (CB blocks of 16 columns):
+//   linear: output columns n0 + 16 cb + r, n0 = chunk * 64 CB + wave * 16 CB
+//   swiglu: blocks [0, CB/2) gate, [CB/2, CB) up, same output columns
+//           n0 + 16 (cb mod CB/2) + r with n0 = chunk * 32 CB + wave * 8 CB
+template <int MB, int CB, int EPI, bool SPLIT>
+__global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
+    constexpr int BM = 16 * MB;
+    constexpr int HALF = CB / 2;
+    __shared__ __attribute__((aligned(16))) uint16_t As[BM][kDAStride];
+
+    const long L = xcd_logical_block(a.per_xcd);
+    if (L >= a.n_logical) return;
+    const int ks = (int)(L % a.ksplit);
+    const long rest = L / a.ksplit;
+    const int nc = (int)(rest % a.n_chunks);
+    const int tm = (int)(rest / a.n_chunks);
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int r = lane & 15;
+    const int j = lane >> 4;
+    const int K = a.K;
+    const int m0 = tm * BM;
+    const int rows = min(BM, a.M - m0);
+    const int nch = K / kDKC;
+    const int c_beg = (int)((long)nch * ks / a.ksplit);
+    const int c_end = (int)((long)nch * (ks + 1) / a.ksplit);
+
+    int n0;
+    const uint16_t* wrow[CB];
+    bool wave_on;
+    if (EPI == EPI_SWIGLU) {
+        n0 = nc * 32 * CB + wave * 8 * CB;
+        wave_on = n0 < a.N0;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int n = min(n0 + 16 * (cb % HALF) + r, a.N0 - 1);
+            wrow[cb] = (cb < HALF ? a.w0 : a.w1) + (size_t)n * K;
+        }
+    } else {
+        n0 = nc * 64 * CB + wave * 16 * CB;
+        wave_on = n0 < a.N0;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int n = min(n0 + 16 * cb + r, a.N0 - 1);
+            wrow[cb] = a.w0 + (size_t)n * K;
+        }
+    }
+    const int active_mb = (rows + 15) >> 4;
+
+    constexpr int A_ITERS = (BM * 16 + 255) / 256;
+    u32x4_t Aq[A_ITERS];
+    auto load_A = [&](int c) {
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it) {
+            const int lin = it * 256 + tid;
+            const int row = lin >> 4, piece = lin & 15;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (row < rows) v = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)(m0 + row) * K + c * kDKC + piece * 8);
+            Aq[it] = v;
+        }
+    };
+    auto store_A = [&]() {
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it) {
+            const int lin = it * 256 + tid;
+            const int row = lin >> 4, piece = lin & 15;
+            if (row < BM) *reinterpret_cast<u32x4_t*>(&As[row][piece * 8]) = Aq[it];
+        }
+    };
+
+    f32x4_t acc[MB][CB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    load_A(c_beg);
+    store_A();
+    __syncthreads();
+    for (int c = c_beg; c < c_end; ++c) {
+        if (c + 1 < c_end) load_A(c + 1);
+        if (wave_on) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x8_t bfr[CB];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    bfr[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
+                                                               wrow[cb] + c * kDKC + 32 * g + 8 * j));
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    if (mb < active_mb) {
+                        const bf16x8_t af = __builtin_bit_cast(
+                            bf16x8_t, *reinterpret_cast<const u32x4_t*>(&As[16 * mb + r][32 * g + 8 * j]));
+#pragma unroll
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[cb], acc[mb][cb], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (c + 1 < c_end) store_A();
+        __syncthreads();
+    }
+    if (!wave_on) return;
+
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if (mb >= active_mb) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rl = 16 * mb + 4 * j + i;
+            if (rl >= rows) continue;
+            const size_t m = (size_t)(m0 + rl);
+            if (SPLIT) {
+                float* prow = a.part + ((size_t)ks * a.M + m) * a.Ntot;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    int col;
+                    if (EPI == EPI_SWIGLU) col = (cb < HALF ? 0 : a.N0) + n0 + 16 * (cb % HALF) + r;
+                    else col = n0 + 16 * cb + r;
+                    if ((EPI == EPI_SWIGLU ? n0 + 16 * (cb % HALF) + r : col) < a.N0) prow[col] = acc[mb][cb][i];
+                }
+            } else if (EPI == EPI_SWIGLU) {
+#pragma unroll
+                for (int p = 0; p < HALF; ++p) {
+                    const int col = n0 + 16 * p + r;
+                    if (col < a.N0) a.y[m * a.N0 + col] = (uint16_t)silu_mul_bits(acc[mb][p][i], acc[mb][HALF + p][i]);
+                }
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    const int col = n0 + 16 * cb + r;
+                    if (col < a.N0) {
+                        uint32_t yb = f32_to_bf16_bits(acc[mb][cb][i]);
+                        if (a.add) yb = add_bits(yb, a.add[m * a.N0 + col]);
+                        a.y[m * a.N0 + col] = (uint16_t)yb;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Sum the split-K partials in ascending split order, then the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_dense_reduce(const float* __restrict__ part, int ksplit, int M,
+                                                      int N0, int Ntot, const uint16_t* __restrict__ add,
+                                                      uint16_t* __restrict__ y) {
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)M * N0) return;
+    const long m = idx / N0;
+    const int n = (int)(idx % N0);
+    if (EPI == EPI_SWIGLU) {
+        float g = 0.0f, u = 0.0f;
+        for (int s = 0; s < ksplit; ++s) {
+            const float* prow = part + ((size_t)s * M + m) * Ntot;
+            g = g + prow[n];
+            u = u + prow[N0 + n];
+        }
+        y[idx] = (uint16_t)silu_mul_bits(g, u);
+    } else {
+        float v = 0.0f;
+        for (int s = 0; s < ksplit; ++s) v = v + part[((size_t)s * M + m) * Ntot + n];
+        uint32_t yb = f32_to_bf16_bits(v);
+        if (add) yb = add_bits(yb, add[idx]);
+        y[idx] = (uint16_t)yb;
+    }
+}
+
+struct Plan {
+    int mb, cb, ksplit, tiles_m, n_chunks;
+};
+
+// Tile shape and split: wide tiles for many rows, narrow tiles plus a K split
+// for few rows (the weights then stream once and ~256+ workgroups fill the GPU).
+Plan plan_dense(int M, int Ntot_cols, int K, bool swiglu) {
+    Plan p{};
+    const int nch = K / kDKC;
+    if (M <= 64) {
+        p.mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+        p.cb = 2;
+    } else {
+        p.mb = M <= 512 ? 4 : 8;
+        p.cb = 4;
+    }
+    const int cols_per_wg = swiglu ? 4 * 8 * p.cb : 4 * 16 * p.cb;  // output columns per workgroup
+    const int N0 = swiglu ? Ntot_cols / 2 : Ntot_cols;
+    p.tiles_m = (M + 16 * p.mb - 1) / (16 * p.mb);
+    p.n_chunks = (N0 + cols_per_wg - 1) / cols_per_wg;
+    p.ksplit = 1;
+    const long blocks = (long)p.tiles_m * p.n_chunks;
+    if (M <= 64) {
+        while (p.ksplit < 8 && blocks * p.ksplit < 256 && nch / (p.ksplit * 2) >= 2) p.ksplit *= 2;
+    }
+    return p;
+}
+
+template <int EPI, bool SPLIT>
+void launch_dense_mb_cb(const Plan& p, DenseArgs& a, hipStream_t st) {
+    const dim3 grid(8 * a.per_xcd), block(256);
+#define MOE_DENSE_CASE(MBv, CBv)                                                                 \
+    if (p.mb == MBv && p.cb == CBv) {                                                            \
+        hipLaunchKernelGGL((k_dense<MBv, CBv, EPI, SPLIT>), grid, block, 0, st, a);              \
+        return;                                                                                  \
+    }
+    MOE_DENSE_CASE(1, 2)
+    MOE_DENSE_CASE(2, 2)
+    MOE_DENSE_CASE(4, 2)
+    MOE_DENSE_CASE(4, 4)
+    MOE_DENSE_CASE(8, 4)
+#undef MOE_DENSE_CASE
+}
+
+int run_dense(int epi, const uint16_t* x, const uint16_t* w0, const uint16_t* w1, const uint16_t* add,
+              uint16_t* y, int M, int N0, int K, void* ws, size_t ws_bytes, hipStream_t st,
+              const char* what) {
+    const bool sw = epi == EPI_SWIGLU;
+    const int Ntot = sw ? 2 * N0 : N0;
+    const Plan p = plan_dense(M, Ntot, K, sw);
+    DenseArgs a{};
+    a.x = x;
+    a.w0 = w0;
+    a.w1 = w1;
+    a.add = add;
+    a.y = y;
+    a.M = M;
+    a.N0 = N0;
+    a.K = K;
+    a.Ntot = Ntot;
+    a.tiles_m = p.tiles_m;
+    a.n_chunks = p.n_chunks;
+    a.ksplit = p.ksplit;
+    a.n_logical = (long)p.tiles_m * p.n_chunks * p.ksplit;
+    a.per_xcd = moe::per_xcd(a.n_logical);
+    if (p.ksplit > 1) {
+        const size_t need = (size_t)p.ksplit * M * Ntot * sizeof(float);
+        if (!ws || ws_bytes < need)
+            return moe::fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, ws_bytes, need);
+        a.part = static_cast<float*>(ws);
+        if (sw) launch_dense_mb_cb<EPI_SWIGLU, true>(p, a, st);
+        else launch_dense_mb_cb<EPI_LINEAR, true>(p, a, st);
+        if (int rc = moe::launch_status(what)) return rc;
+        const long n = (long)M * N0;
+        const dim3 g((unsigned)((n + 255) / 256));
+        if (sw) hipLaunchKernelGGL(k_dense_reduce<EPI_SWIGLU>, g, dim3(256), 0, st, a.part, p.ksplit, M, N0, Ntot, nullptr, y);
+        else hipLaunchKernelGGL(k_dense_reduce<EPI_LINEAR>, g, dim3(256), 0, st, a.part, p.ksplit, M, N0, Ntot, add, y);
+        return moe::launch_status(what);
+    }
+    if (sw) launch_dense_mb_cb<EPI_SWIGLU, false>(p, a, st);
+    else launch_dense_mb_cb<EPI_LINEAR, false>(p, a, st);
+    return moe::launch_status(what);
+}
+
+__global__ __launch_bounds__(256) void k_silu_mul(const uint16_t* __restrict__ g, const uint16_t* __restrict__ u,
+                                                  uint16_t* __restrict__ h, long n) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(g[i])));
+    h[i] = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(u[i]));
+}
+
+// One workgroup per row: fp32 mean square (tree order), r = 1/sqrt(ms + eps),
+// y = bf16(bf16(x r) * gain).
+__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gain,
+                                                 float eps, uint16_t* __restrict__ y, int N) {
+    __shared__ float red[4];
+    const uint16_t* xr = x + (size_t)blockIdx.x * N;
+    float ss = 0.0f;
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        const float v = bf16_bits_to_f32(xr[i]);
+        ss = ss + v * v;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off);
+    if (lane_id() == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float rr = 1.0f / __builtin_sqrtf(tot / (float)N + eps);
+    uint16_t* yr = y + (size_t)blockIdx.x * N;
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        const uint32_t nb = f32_to_bf16_bits(bf16_bits_to_f32(xr[i]) * rr);
+        yr[i] = (uint16_t)f32_to_bf16_bits(bf16_bits_to_f32(nb) * bf16_bits_to_f32(gain[i]));
+    }
+}
+
+}  // namespace
+
+extern "C" size_t moe_dense_workspace_bytes(int M, int N_total, int K) {
+    if (M <= 0 || N_total <= 0 || K <= 0 || K % kDKC) return 0;
+    // both epilogues share the plan shape rules; take the larger split
+    const Plan pl = plan_dense(M, N_total, K, false);
+    const Plan ps = plan_dense(M, N_total, K, true);
+    const int ks = pl.ksplit > ps.ksplit ? pl.ksplit : ps.ksplit;
+    return ks > 1 ? (size_t)ks * M * N_total * sizeof(float) : 0;
+}
+
+extern "C" int moe_linear_bf16(const uint16_t* x, const uint16_t* w, const uint16_t* add, uint16_t* y,
+                               int M, int N, int K, void* ws, size_t ws_bytes, void* stream) {
+    using namespace moe;
+    const char* what = "moe_linear_bf16";
+    if (M < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes", what);
+    if (N % 64 || K % kDKC) return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d (x64) K=%d (x128)", what, N, K);
+    if (M == 0) return MOE_OK;
+    if (!x || !w || !y) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    if (!aligned16(x) || !aligned16(w)) return fail(MOE_ERR_INVALID_ARG, "%s: x, w must be 16-byte aligned", what);
+    return run_dense(EPI_LINEAR, x, w, nullptr, add, y, M, N, K, ws, ws_bytes, as_stream(stream), what);
+}
+
+extern "C" int moe_dense_swiglu_bf16(const uint16_t* x, const uint16_t* w_gate, const uint16_t* w_up,
+                                     uint16_t* h, int M, int H, int I, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    using namespace moe;
+    const char* what = "moe_dense_swiglu_bf16";
+    if (M < 0 || H <= 0 || I <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes", what);
+    if (I % 64 || H % kDKC) return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d (x64) H=%d (x128)", what, I, H);
+    if (M == 0) return MOE_OK;
+    if (!x || !w_gate || !w_up || !h) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up))
+        return fail(MOE_ERR_INVALID_ARG, "%s: x and weights must be 16-byte aligned", what);
+    return run_dense(EPI_SWIGLU, x, w_gate, w_up, nullptr, h, M, I, H, ws, ws_bytes, as_stream(stream), what);
+}
+
+extern "C" int moe_silu_mul_bf16(const uint16_t* g, const uint16_t* u, uint16_t* h, int64_t n, void* stream) {
+    using namespace moe;
+    if (n < 0) return fail(MOE_ERR_INVALID_ARG, "moe_silu_mul_bf16: n=%lld", (long long)n);
+    if (n == 0) return MOE_OK;
+    if (!g || !u || !h) return fail(MOE_ERR_INVALID_ARG, "moe_silu_mul_bf16: null pointer");
+    hipLaunchKernelGGL(k_silu_mul, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, as_stream(stream), g, u, h, (long)n);
+    return launch_status("moe_silu_mul_bf16");
+}
+
+extern "C" int moe_rmsnorm_bf16(const uint16_t* x, const uint16_t* gain, float eps, uint16_t* y, int M, int N,
+                                void* stream) {
+    using namespace moe;
+    if (M < 0 || N <= 0 || !(eps >= 0.0f)) return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm_bf16: bad sizes/eps");
+    if (M == 0) return MOE_OK;
+    if (!x || !gain || !y) return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm_bf16: null pointer");
+    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, as_stream(stream), x, gain, eps, y, N);
+    return launch_status("moe_rmsnorm_bf16");
+}

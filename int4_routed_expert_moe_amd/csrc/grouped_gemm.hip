@@ -1,0 +1,539 @@
+// Grouped int4 expert GEMMs over the ragged expert segments ("Kimi
+// exact-generator adaptation": routed gate/up/down as packed int4 with group-32
+// scales, "The preserved forward form"; "Kimi K2.5 donor reference", record
+// "SwiGLU-style gated feed-forward projection"; "Kimi-K3 latent MoE" page,
+// Code: the per-expert loop of moe_infer, here one launch for all experts).
+//
+// Work item = (tile, column chunk).  A tile is up to 16*MB consecutive rows of
+// one expert's segment of the permuted slot list; its expert and first row
+// come from the device-side offsets (no host synchronisation; the grid is
+// sized for the worst case and surplus blocks exit).  A workgroup is 4 waves;
+// each wave owns 64 weight rows (4 column blocks of 16) and all tile rows.
+//
+// Matrix cores: v_mfma_f32_16x16x32_f16.  Weights are dequantised in
+// registers to fp16 q*s: a nibble is moved to bits 6..9 of a half, its sign
+// bit flipped and an exponent OR-ed in (the half is then 16 + q + 8), and one
+// packed fma with (s, -24 s) gives q*s exactly (q*s has at most 11 significant
+// bits; s and 24 s are exact in fp16 for scales in [2^-14, 2^9]).  Two weights
+// per packed op; the half pairs hold elements (p, p+4) of an 8-element block,
+// and the activation tile in LDS is stored with the same in-block order.
+//
+// bf16 mode: activations are converted to fp16 when staged (exact for
+// |x| < 65504 away from fp16 subnormals) and each lane's 16-byte weight load
+// covers one scale group; the 4 matrix-core steps of a 128-wide K chunk take
+// one packed dword from each of the 4 groups, and A is read to match, so all
+// of K accumulates in one fp32 accumulator.
+// Exact mode: int8 activations are exact fp16 integers and each matrix-core
+// step covers exactly one scale group, so its result is s_w * G with G the
+// exact int32 group sum (every partial sum is an integer multiple of the
+// scale's last-bit weight below 2^24, hence exact in fp32); the group result is
+// folded into the row's accumulator as fma(s_w*G, s_x, acc), groups ascending.
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kKC = 128;        // K elements per chunk (4 scale groups)
+constexpr int kAStride = 136;   // halves per LDS activation row (128 + 8 pad)
+
+struct GroupedArgs {
+    const void* act;        // bf16 or int8 [rows][K]
+    const float* act_scale; // exact: [rows][K/32]
+    const uint8_t* w0;      // gate (gate/up) or down
+    const uint16_t* s0;
+    const uint8_t* w1;      // up (gate/up only)
+    const uint16_t* s1;
+    const int32_t* offsets;
+    const int32_t* sorted_slot;
+    int k;
+    int E;
+    int K;
+    int N;          // output columns per matrix
+    int n_chunks;   // column chunks per tile
+    long n_logical; // tile bound * n_chunks
+    int per_xcd;
+    void* out;
+    float* out_scale;
+};
+
+struct TileInfo {
+    int e;
+    int row0;   // first sorted position of the tile
+    int rows;   // rows in the tile (1..16*MB)
+};
+
+// Locate tile `tile` in the concatenation over experts of ceil(count_e / bm)
+// tiles each.  Every wave computes it; the result is wave-uniform.
+__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bm, long tile,
+                          TileInfo& ti) {
+    const int lane = lane_id();
+    long base = 0;
+    for (int c0 = 0; c0 < E; c0 += MOE_WAVE) {
+        const int e = c0 + lane;
+        int beg = 0, cnt = 0;
+        if (e < E) {
+            beg = offsets[e];
+            cnt = offsets[e + 1] - beg;
+        }
+        const int nt = (cnt + bm - 1) / bm;
+        int incl = nt;
+#pragma unroll
+        for (int d = 1; d < MOE_WAVE; d <<= 1) {
+            const int v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+        }
+        const int total = __shfl(incl, MOE_WAVE - 1);
+        if (tile < base + total) {
+            const int excl = incl - nt;
+            const bool mine = (tile >= base + excl) && (tile < base + incl);
+            const uint64_t m = __ballot(mine);
+            const int src = __ffsll((unsigned long long)m) - 1;
+            const int j = (int)(tile - base - __shfl(excl, src));
+            const int sb = __shfl(beg, src), sc = __shfl(cnt, src);
+            ti.e = __shfl(e, src);
+            ti.row0 = sb + j * bm;
+            ti.rows = min(bm, sc - j * bm);
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// 8 int4 weights of one packed dword (element p in nibble p) -> fp16 q*s,
+// ordered (e0, e4, e1, e5, e2, e6, e3, e7).
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2, half2_t c2) {
+    const uint32_t M = 0x03C003C0u;  // bits 6..9 of each half
+    const uint32_t X = 0x4E004E00u;  // flips the nibble's sign bit, sets the exponent of 16
+    const uint32_t t0 = ((w << 6) & M) ^ X;
+    const uint32_t t1 = ((w << 2) & M) ^ X;
+    const uint32_t t2 = ((w >> 2) & M) ^ X;
+    const uint32_t t3 = ((w >> 6) & M) ^ X;
+    const half2_t h0 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, t0), s2, c2);
+    const half2_t h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, t1), s2, c2);
+    const half2_t h2 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, t2), s2, c2);
+    const half2_t h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, t3), s2, c2);
+    half8_t r;
+    r[0] = h0[0]; r[1] = h0[1];
+    r[2] = h1[0]; r[3] = h1[1];
+    r[4] = h2[0]; r[5] = h2[1];
+    r[6] = h3[0]; r[7] = h3[1];
+    return r;
+}
+
+// bf16 scale bits -> (s, s) and (-24 s, -24 s) in fp16.
+__device__ __forceinline__ void scale_pair(uint32_t sbits, half2_t& s2, half2_t& c2) {
+    const float s = bf16_bits_to_f32(sbits & 0xFFFFu);
+    const _Float16 sh = (_Float16)s;
+    const _Float16 ch = (_Float16)(-24.0f * s);
+    s2 = half2_t{sh, sh};
+    c2 = half2_t{ch, ch};
+}
+
+// 8 bf16 (4 dwords, elements in order) -> 8 fp16 in the (p, p+4) pair order.
+__device__ __forceinline__ u32x4_t bf16x8_to_f16_perm(u32x4_t d) {
+    const float f0 = __uint_as_float(d[0] << 16), f1 = __uint_as_float(d[0] & 0xFFFF0000u);
+    const float f2 = __uint_as_float(d[1] << 16), f3 = __uint_as_float(d[1] & 0xFFFF0000u);
+    const float f4 = __uint_as_float(d[2] << 16), f5 = __uint_as_float(d[2] & 0xFFFF0000u);
+    const float f6 = __uint_as_float(d[3] << 16), f7 = __uint_as_float(d[3] & 0xFFFF0000u);
+    u32x4_t r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f0, f4));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f1, f5));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f2, f6));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f3, f7));
+    return r;
+}
+
+// 8 int8 (2 dwords, elements in order) -> 8 exact fp16 integers in pair order.
+__device__ __forceinline__ u32x4_t i8x8_to_f16_perm(uint32_t d0, uint32_t d1) {
+    u32x4_t r;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + p) << 16) | (uint32_t)p;
+        uint32_t t = __builtin_amdgcn_perm(d1, d0, sel);       // (e_p, e_{p+4}) in the low bytes
+        t = (t ^ 0x00800080u) | 0x64006400u;                    // fp16 1024 + (q + 128)
+        const half2_t h = __builtin_bit_cast(half2_t, t) + half2_t{(_Float16)-1152.0f, (_Float16)-1152.0f};
+        r[p] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+}
+
+template <int MODE, int OP, int MB>
+__global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
+    constexpr int BM = 16 * MB;
+    constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
+    constexpr bool GATEUP = OP == 0;
+    // activation staging: bf16 rows are 16 pieces of 16 B per chunk, int8 rows 8
+    constexpr int PIECES = EXACT ? 8 : 16;
+    constexpr int A_ITERS = (BM * PIECES + 255) / 256;
+
+    __shared__ __attribute__((aligned(16))) _Float16 As[BM][kAStride];
+    __shared__ __attribute__((aligned(16))) float SX[EXACT ? 4 : 1][EXACT ? BM : 1];
+    __shared__ int32_t rowsrc[BM];
+
+    const long L = xcd_logical_block(a.per_xcd);
+    if (L >= a.n_logical) return;
+    const long tile = L / a.n_chunks;
+    const int nc = (int)(L % a.n_chunks);
+    TileInfo ti;
+    if (!find_tile(a.offsets, a.E, BM, tile, ti)) return;
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int r = lane & 15;   // row/column within a 16-block
+    const int j = lane >> 4;   // k-block of the lane (0..3)
+    const int K = a.K;
+    const int N = a.N;
+    const int nch = K / kKC;
+
+    if (tid < BM) {
+        int src = -1;
+        if (tid < ti.rows) src = GATEUP ? a.sorted_slot[ti.row0 + tid] / a.k : ti.row0 + tid;
+        rowsrc[tid] = src;
+    }
+
+    // this wave's weight rows, per column block
+    const uint8_t* wrow[4];
+    const uint16_t* srow[4];
+    const size_t wmat = (size_t)N * (size_t)(K / 2);
+    const size_t smat = (size_t)N * (size_t)(K / 32);
+    int n0;
+    if (GATEUP) {
+        n0 = nc * 128 + wave * 32;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int n = n0 + 16 * (cb & 1) + r;
+            const uint8_t* wb = (cb < 2 ? a.w0 : a.w1) + (size_t)ti.e * wmat;
+            const uint16_t* sb = (cb < 2 ? a.s0 : a.s1) + (size_t)ti.e * smat;
+            wrow[cb] = wb + (size_t)n * (K / 2);
+            srow[cb] = sb + (size_t)n * (K / 32);
+        }
+    } else {
+        n0 = nc * 256 + wave * 64;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int n = n0 + 16 * cb + r;
+            wrow[cb] = a.w0 + (size_t)ti.e * wmat + (size_t)n * (K / 2);
+            srow[cb] = a.s0 + (size_t)ti.e * smat + (size_t)n * (K / 32);
+        }
+    }
+    __syncthreads();  // rowsrc visible
+
+    const int active_mb = (ti.rows + 15) >> 4;
+
+    // ---- prefetch registers ----
+    u32x4_t Bq[4];       // bf16 mode: one 16-byte group per column block; exact: 4 dwords (groups 0..3)
+    uint32_t Sq[4][2];   // bf16 mode: Sq[cb][0] = scale bits; exact: 4 bf16 scales
+    u32x4_t Aq[A_ITERS];
+    f32x4_t SXq = {0.f, 0.f, 0.f, 0.f};
+
+    auto load_B = [&](int c) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            if (!EXACT) {
+                Bq[cb] = *reinterpret_cast<const u32x4_t*>(wrow[cb] + (size_t)c * 64 + 16 * j);
+                Sq[cb][0] = srow[cb][c * 4 + j];
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    Bq[cb][g] = *reinterpret_cast<const uint32_t*>(wrow[cb] + (size_t)c * 64 + 16 * g + 4 * j);
+                const u32x2_t s = *reinterpret_cast<const u32x2_t*>(srow[cb] + c * 4);
+                Sq[cb][0] = s[0];
+                Sq[cb][1] = s[1];
+            }
+        }
+    };
+    auto load_A = [&](int c) {
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it) {
+            const int lin = it * 256 + tid;
+            const int row = lin / PIECES;
+            const int piece = lin % PIECES;
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (row < BM) {
+                const int src = rowsrc[row];
+                if (src >= 0) {
+                    if (!EXACT) {
+                        const uint16_t* p = static_cast<const uint16_t*>(a.act) + (size_t)src * K + c * kKC + piece * 8;
+                        v = *reinterpret_cast<const u32x4_t*>(p);
+                    } else {
+                        const int8_t* p = static_cast<const int8_t*>(a.act) + (size_t)src * K + c * kKC + piece * 16;
+                        v = *reinterpret_cast<const u32x4_t*>(p);
+                    }
+                }
+            }
+            Aq[it] = v;
+        }
+        if (EXACT && tid < BM) {
+            const int src = rowsrc[tid];
+            SXq = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (src >= 0) SXq = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)src * (K / 32) + c * 4);
+        }
+    };
+    auto store_A = [&]() {
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it) {
+            const int lin = it * 256 + tid;
+            const int row = lin / PIECES;
+            const int piece = lin % PIECES;
+            if (row < BM) {
+                if (!EXACT) {
+                    *reinterpret_cast<u32x4_t*>(&As[row][piece * 8]) = bf16x8_to_f16_perm(Aq[it]);
+                } else {
+                    *reinterpret_cast<u32x4_t*>(&As[row][piece * 16]) = i8x8_to_f16_perm(Aq[it][0], Aq[it][1]);
+                    *reinterpret_cast<u32x4_t*>(&As[row][piece * 16 + 8]) = i8x8_to_f16_perm(Aq[it][2], Aq[it][3]);
+                }
+            }
+        }
+        if (EXACT && tid < BM) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) SX[g][tid] = SXq[g];
+        }
+    };
+
+    f32x4_t acc[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    load_B(0);
+    load_A(0);
+    store_A();
+    __syncthreads();
+
+    for (int c = 0; c < nch; ++c) {
+        u32x4_t Bc[4];
+        uint32_t Sc[4][2];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            Bc[cb] = Bq[cb];
+            Sc[cb][0] = Sq[cb][0];
+            Sc[cb][1] = Sq[cb][1];
+        }
+        if (c + 1 < nch) {
+            load_B(c + 1);
+            load_A(c + 1);
+        }
+        if (!EXACT) {
+            half2_t s2[4], c2[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) scale_pair(Sc[cb][0], s2[cb], c2[cb]);
+#pragma unroll
+            for (int gp = 0; gp < 4; ++gp) {
+                half8_t bf[4];
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) bf[cb] = dequant8(Bc[cb][gp], s2[cb], c2[cb]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    if (mb < active_mb) {
+                        const half8_t af = *reinterpret_cast<const half8_t*>(&As[16 * mb + r][32 * j + 8 * gp]);
+#pragma unroll
+                        for (int cb = 0; cb < 4; ++cb)
+                            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                half8_t bf[4];
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    half2_t s2, c2;
+                    scale_pair(Sc[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
+                    bf[cb] = dequant8(Bc[cb][g], s2, c2);
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    if (mb < active_mb) {
+                        const half8_t af = *reinterpret_cast<const half8_t*>(&As[16 * mb + r][32 * g + 8 * j]);
+                        const f32x4_t sx = *reinterpret_cast<const f32x4_t*>(&SX[g][16 * mb + 4 * j]);
+#pragma unroll
+                        for (int cb = 0; cb < 4; ++cb) {
+                            const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                af, bf[cb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[mb][cb][i] = __builtin_fmaf(d[i], sx[i], acc[mb][cb][i]);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (c + 1 < nch) store_A();
+        __syncthreads();
+    }
+
+    // ---- epilogue ----
+    if (GATEUP) {
+        const int grp = n0 / 32;  // this wave's 32 output columns form one scale group
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (mb >= active_mb) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = 16 * mb + 4 * j + i;
+                const bool ok = rl < ti.rows;
+                const size_t orow = (size_t)(ti.row0 + rl);
+                if (!EXACT) {
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        const uint32_t gb = f32_to_bf16_bits(acc[mb][p][i]);
+                        const uint32_t ub = f32_to_bf16_bits(acc[mb][2 + p][i]);
+                        const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
+                        const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
+                        if (ok) static_cast<uint16_t*>(a.out)[orow * N + n0 + 16 * p + r] = (uint16_t)hb;
+                    }
+                } else {
+                    const float h0 = moe_silu(acc[mb][0][i]) * acc[mb][2][i];
+                    const float h1 = moe_silu(acc[mb][1][i]) * acc[mb][3][i];
+                    float amax = fmaxf(fabsf(h0), fabsf(h1));
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+                    const float s = (amax == 0.0f) ? 0.0f : amax / 127.0f;
+                    if (ok) {
+                        int8_t* o = static_cast<int8_t*>(a.out) + orow * N + n0 + r;
+                        o[0] = (int8_t)moe_quant_i8(h0, s);
+                        o[16] = (int8_t)moe_quant_i8(h1, s);
+                        if (r == 0) a.out_scale[orow * (N / 32) + grp] = s;
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (mb >= active_mb) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = 16 * mb + 4 * j + i;
+                if (rl >= ti.rows) continue;
+                const size_t orow = (size_t)(ti.row0 + rl);
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    const int col = n0 + 16 * cb + r;
+                    if (!EXACT)
+                        static_cast<uint16_t*>(a.out)[orow * N + col] = (uint16_t)f32_to_bf16_bits(acc[mb][cb][i]);
+                    else
+                        static_cast<float*>(a.out)[orow * N + col] = acc[mb][cb][i];
+                }
+            }
+        }
+    }
+}
+
+// Rows per tile: as many 16-row blocks as an average expert segment needs.
+int pick_mb(int S, int E) {
+    const double avg = (double)S / (double)E;
+    if (avg <= 12.0) return 1;
+    if (avg <= 24.0) return 2;
+    if (avg <= 48.0) return 4;
+    return 8;
+}
+
+template <int MODE, int OP>
+int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
+    const int mb = pick_mb(S, a.E);
+    const int bm = 16 * mb;
+    const long tiles = ((long)S + (long)a.E * (bm - 1)) / bm + 1;
+    a.n_logical = tiles * a.n_chunks;
+    a.per_xcd = moe::per_xcd(a.n_logical);
+    const dim3 grid(8 * a.per_xcd), block(256);
+    switch (mb) {
+    case 1: hipLaunchKernelGGL((k_grouped<MODE, OP, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_grouped<MODE, OP, 2>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_grouped<MODE, OP, 4>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_grouped<MODE, OP, 8>), grid, block, 0, st, a); break;
+    }
+    return moe::launch_status(what);
+}
+
+int check_common(const char* what, int mode, int T, int k, int E) {
+    using namespace moe;
+    if (mode != MOE_MODE_BF16 && mode != MOE_MODE_EXACT_I8)
+        return fail(MOE_ERR_INVALID_ARG, "%s: mode %d", what, mode);
+    if (T < 0 || k <= 0 || E <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes", what);
+    if (E > 1024 || k > 16 || k > E || (long)T * k >= (1L << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d k=%d T=%d outside limits", what, E, k, T);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_int4_grouped_swiglu(int mode, const void* act, const float* act_scale,
+                                       const uint8_t* gate_packed, const uint16_t* gate_scale,
+                                       const uint8_t* up_packed, const uint16_t* up_scale,
+                                       const int32_t* offsets, const int32_t* sorted_slot, int T,
+                                       int k, int E, int H, int I, void* h, float* h_scale,
+                                       void* stream) {
+    using namespace moe;
+    const char* what = "moe_int4_grouped_swiglu";
+    if (int rc = check_common(what, mode, T, k, E)) return rc;
+    if (H <= 0 || I <= 0 || H % kKC != 0 || I % 128 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: H=%d (multiple of 128) I=%d (multiple of 128)", what, H, I);
+    if (T == 0) return MOE_OK;
+    if (!act || !gate_packed || !gate_scale || !up_packed || !up_scale || !offsets || !sorted_slot || !h)
+        return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    const bool exact = mode == MOE_MODE_EXACT_I8;
+    if (exact && (!act_scale || !h_scale))
+        return fail(MOE_ERR_INVALID_ARG, "%s: exact mode needs act_scale and h_scale", what);
+    if (!exact && (act_scale || h_scale))
+        return fail(MOE_ERR_INVALID_ARG, "%s: bf16 mode takes no scales", what);
+    if (!aligned16(act) || !aligned16(gate_packed) || !aligned16(up_packed) ||
+        (exact && !aligned16(act_scale)))
+        return fail(MOE_ERR_INVALID_ARG, "%s: activations and packed weights must be 16-byte aligned", what);
+    GroupedArgs a{};
+    a.act = act;
+    a.act_scale = act_scale;
+    a.w0 = gate_packed;
+    a.s0 = gate_scale;
+    a.w1 = up_packed;
+    a.s1 = up_scale;
+    a.offsets = offsets;
+    a.sorted_slot = sorted_slot;
+    a.k = k;
+    a.E = E;
+    a.K = H;
+    a.N = I;
+    a.n_chunks = I / 128;
+    a.out = h;
+    a.out_scale = h_scale;
+    hipStream_t st = as_stream(stream);
+    return exact ? launch_grouped<MOE_MODE_EXACT_I8, 0>(a, T * k, st, what)
+                 : launch_grouped<MOE_MODE_BF16, 0>(a, T * k, st, what);
+}
+
+extern "C" int moe_int4_grouped_down(int mode, const void* h, const float* h_scale,
+                                     const uint8_t* down_packed, const uint16_t* down_scale,
+                                     const int32_t* offsets, int T, int k, int E, int I, int H,
+                                     void* y, void* stream) {
+    using namespace moe;
+    const char* what = "moe_int4_grouped_down";
+    if (int rc = check_common(what, mode, T, k, E)) return rc;
+    if (H <= 0 || I <= 0 || I % kKC != 0 || H % 256 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d (multiple of 128) H=%d (multiple of 256)", what, I, H);
+    if (T == 0) return MOE_OK;
+    if (!h || !down_packed || !down_scale || !offsets || !y)
+        return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    const bool exact = mode == MOE_MODE_EXACT_I8;
+    if (exact && !h_scale) return fail(MOE_ERR_INVALID_ARG, "%s: exact mode needs h_scale", what);
+    if (!exact && h_scale) return fail(MOE_ERR_INVALID_ARG, "%s: bf16 mode takes no scales", what);
+    if (!aligned16(h) || !aligned16(down_packed) || (exact && !aligned16(h_scale)))
+        return fail(MOE_ERR_INVALID_ARG, "%s: activations and packed weights must be 16-byte aligned", what);
+    GroupedArgs a{};
+    a.act = h;
+    a.act_scale = h_scale;
+    a.w0 = down_packed;
+    a.s0 = down_scale;
+    a.offsets = offsets;
+    a.k = k;
+    a.E = E;
+    a.K = I;
+    a.N = H;
+    a.n_chunks = H / 256;
+    a.out = y;
+    hipStream_t st = as_stream(stream);
+    return exact ? launch_grouped<MOE_MODE_EXACT_I8, 1>(a, T * k, st, what)
+                 : launch_grouped<MOE_MODE_BF16, 1>(a, T * k, st, what);
+}

@@ -1,0 +1,169 @@
+"""One MoE layer forward as a sequence of C-ABI calls on one HIP stream.
+
+Kimi-K3 latent MoE page, Code (forward / moe_infer): the router sees the
+full-width hidden state; the latent variant projects it down before the
+routed experts and back up after an RMSNorm; the shared expert runs on the
+full-width input and is added last.  For the K2.5-shaped layer there is no
+latent step and the shared add happens inside the combine.
+
+Nothing here computes: the class owns device buffers (weights and a
+per-token-count workspace) and issues the library calls in order.  No call
+synchronises with the host.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import moe as _m
+
+
+def _bf16(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def _u8(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class MoELayer:
+    """Routed int4 experts + shared bf16 expert (+ optional K3 latent wrapper)."""
+
+    def __init__(self, cfg: dict, router_w, router_b, experts: dict, shared: dict | None = None,
+                 latent: dict | None = None):
+        self.cfg = dict(cfg)
+        self.mode = _m.MOE_MODE_EXACT_I8 if cfg["mode"] == "exact" else _m.MOE_MODE_BF16
+        self.router_w = router_w
+        self.router_b = router_b
+        self.ex = experts
+        self.shared = shared
+        self.latent = latent
+        self.E, self.k, self.H, self.I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
+        self.Kin = cfg.get("L") or cfg["H"]  # width the routed experts see
+        self._ws = {}
+        self.device = router_w.device
+        if self.mode == _m.MOE_MODE_EXACT_I8 and (shared is not None or latent is not None):
+            raise ValueError("exact mode is defined for the routed experts alone")
+
+    @classmethod
+    def from_numpy(cls, inp: dict, device="cuda"):
+        """Upload the generator's numpy arrays (bf16 as uint16 bits)."""
+        cfg = inp["cfg"]
+        ex = inp["experts"]
+        experts = {
+            "wg": _u8(ex["wg"], device), "sg": _bf16(ex["sg"], device),
+            "wu": _u8(ex["wu"], device), "su": _bf16(ex["su"], device),
+            "wd": _u8(ex["wd"], device), "sd": _bf16(ex["sd"], device),
+        }
+        shared = None
+        if inp.get("shared") is not None:
+            shared = {n: _bf16(inp["shared"][n], device) for n in ("wg", "wu", "wd")}
+        latent = None
+        if inp.get("latent") is not None:
+            latent = {n: _bf16(inp["latent"][n], device) for n in ("w_down", "w_up", "gain")}
+        return cls(cfg, _bf16(inp["router_w"], device),
+                   torch.from_numpy(np.ascontiguousarray(inp["router_b"], dtype=np.float32)).to(device),
+                   experts, shared, latent)
+
+    # ------------------------------------------------------------------
+    def workspace(self, T: int) -> dict:
+        """Device buffers for T tokens (allocated once per T and reused)."""
+        if T in self._ws:
+            return self._ws[T]
+        dev, E, k, H, I, Kin = self.device, self.E, self.k, self.H, self.I, self.Kin
+        S = T * k
+        exact = self.mode == _m.MOE_MODE_EXACT_I8
+        w = {
+            "route_ws": torch.empty(max(1, _m.moe_route_workspace_bytes(T, E)), dtype=torch.uint8, device=dev),
+            "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+            "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
+            "counts": torch.empty(E, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "sorted_slot": torch.empty(S, dtype=torch.int32, device=dev),
+            "slot_pos": torch.empty(S, dtype=torch.int32, device=dev),
+            "h": torch.empty((S, I), dtype=torch.int8 if exact else torch.bfloat16, device=dev),
+            "h_scale": torch.empty((S, I // 32), dtype=torch.float32, device=dev) if exact else None,
+            "y": torch.empty((S, Kin), dtype=torch.float32 if exact else torch.bfloat16, device=dev),
+            "out": torch.empty((T, H), dtype=torch.float32 if exact else torch.bfloat16, device=dev),
+        }
+        if exact:
+            w["qx"] = torch.empty((T, Kin), dtype=torch.int8, device=dev)
+            w["sx"] = torch.empty((T, Kin // 32), dtype=torch.float32, device=dev)
+        dense_bytes = 0
+        if self.shared is not None:
+            Is = self.shared["wg"].shape[0]
+            w["shared_h"] = torch.empty((T, Is), dtype=torch.bfloat16, device=dev)
+            w["shared_out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            dense_bytes = max(dense_bytes, _m.moe_dense_workspace_bytes(T, 2 * Is, H),
+                              _m.moe_dense_workspace_bytes(T, H, Is))
+        if self.latent is not None:
+            L = Kin
+            w["x_lat"] = torch.empty((T, L), dtype=torch.bfloat16, device=dev)
+            w["routed"] = torch.empty((T, L), dtype=torch.bfloat16, device=dev)
+            w["normed"] = torch.empty((T, L), dtype=torch.bfloat16, device=dev)
+            dense_bytes = max(dense_bytes, _m.moe_dense_workspace_bytes(T, L, H),
+                              _m.moe_dense_workspace_bytes(T, H, L))
+        w["dense_ws"] = torch.empty(max(1, dense_bytes), dtype=torch.uint8, device=dev)
+        self._ws[T] = w
+        return w
+
+    def forward(self, x: torch.Tensor, marks: list | None = None) -> torch.Tensor:
+        """x [T, H] bf16 -> out [T, H] (bf16, or fp32 in exact mode).  Returns the
+        workspace's output buffer; the intermediates stay in ``workspace(T)``.
+        ``marks``: when a list is given, a timing event on the current stream is
+        appended after every call as (call name, event)."""
+        T = x.shape[0]
+        w = self.workspace(T)
+        if T == 0:
+            return w["out"]
+
+        def mark(name):
+            if marks is not None:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record()
+                marks.append((name, ev))
+
+        mark("start")
+        E, k, H, I, Kin = self.E, self.k, self.H, self.I, self.Kin
+        ex = self.ex
+        _m.moe_route(x, self.router_w, self.router_b, k, True, w["topk_idx"], w["topk_w"], w["route_ws"])
+        mark("moe_route")
+        _m.moe_permute(w["topk_idx"], E, w["counts"], w["offsets"], w["sorted_slot"], w["slot_pos"])
+        mark("moe_permute")
+        act = x
+        if self.latent is not None:
+            _m.moe_linear_bf16(x, self.latent["w_down"], None, w["x_lat"], w["dense_ws"])
+            mark("latent_down")
+            act = w["x_lat"]
+        shared_out = None
+        if self.shared is not None:
+            _m.moe_dense_swiglu_bf16(x, self.shared["wg"], self.shared["wu"], w["shared_h"], w["dense_ws"])
+            mark("shared_gate_up")
+            _m.moe_linear_bf16(w["shared_h"], self.shared["wd"], None, w["shared_out"], w["dense_ws"])
+            mark("shared_down")
+            shared_out = w["shared_out"]
+        if self.mode == _m.MOE_MODE_EXACT_I8:
+            _m.moe_quant_act_int8(act, w["qx"], w["sx"])
+            mark("moe_quant_act_int8")
+            _m.moe_int4_grouped_swiglu(self.mode, w["qx"], w["sx"], ex["wg"], ex["sg"], ex["wu"], ex["su"],
+                                       w["offsets"], w["sorted_slot"], T, k, E, Kin, I, w["h"], w["h_scale"])
+        else:
+            _m.moe_int4_grouped_swiglu(self.mode, act, None, ex["wg"], ex["sg"], ex["wu"], ex["su"],
+                                       w["offsets"], w["sorted_slot"], T, k, E, Kin, I, w["h"], None)
+        mark("moe_int4_grouped_swiglu")
+        _m.moe_int4_grouped_down(self.mode, w["h"], w["h_scale"], ex["wd"], ex["sd"], w["offsets"], T, k, E, I,
+                                 Kin, w["y"])
+        mark("moe_int4_grouped_down")
+        if self.latent is None:
+            _m.moe_combine(self.mode, w["y"], w["slot_pos"], w["topk_w"], shared_out, T, k, H, w["out"])
+            mark("moe_combine")
+        else:
+            _m.moe_combine(self.mode, w["y"], w["slot_pos"], w["topk_w"], None, T, k, Kin, w["routed"])
+            mark("moe_combine")
+            _m.moe_rmsnorm_bf16(w["routed"], self.latent["gain"], self.cfg["rms_eps"], w["normed"])
+            mark("moe_rmsnorm_bf16")
+            _m.moe_linear_bf16(w["normed"], self.latent["w_up"], shared_out, w["out"], w["dense_ws"])
+            mark("latent_up")
+        return w["out"]
+
+    __call__ = forward

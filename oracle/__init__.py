@@ -62,6 +62,8 @@ def _declare(L):
     L.oracle_f32_to_bf16.restype = ctypes.c_uint16
     L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
     L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    L.oracle_threads.argtypes = []
+    L.oracle_threads.restype = I32
     L.oracle_const.argtypes = [I32]
     L.oracle_const.restype = F32
     for name in ("oracle_exp_ref", "oracle_sigmoid_ref", "oracle_silu_ref"):
@@ -114,6 +116,11 @@ def f32_to_bf16(v: float) -> int:
 
 def f64_to_bf16(v: float) -> int:
     return int(lib().oracle_f64_to_bf16(float(v)))
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return int(lib().oracle_threads())
 
 
 def const(which: int) -> float:

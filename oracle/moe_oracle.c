@@ -565,3 +565,15 @@ void oracle_f64_to_bf16_n(const double* d, int n, uint16_t* out) {
 void oracle_f32_to_bf16_n(const float* f, int n, uint16_t* out) {
     for (int i = 0; i < n; ++i) out[i] = f32_to_bf16(f[i]);
 }
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+/* Number of threads the oracle's parallel loops use. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

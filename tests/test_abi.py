@@ -1,0 +1,102 @@
+"""The C-ABI library loads on a host without a GPU, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_int4.h")
+LIB = os.path.join(ROOT, "int4_routed_expert_moe_amd", "libmoe_int4.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from int4_routed_expert_moe_amd import build
+        build.build(verbose=False)
+    return ctypes.CDLL(LIB)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_layer_calls():
+    names = _declared()
+    for n in ("moe_route", "moe_permute", "moe_int4_grouped_swiglu", "moe_int4_grouped_down", "moe_combine",
+              "moe_linear_bf16", "moe_rmsnorm_bf16", "moe_quant_act_int8"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_header():
+    from int4_routed_expert_moe_amd import moe
+    assert sorted(moe.EXPORTS) == _declared()
+    for n in _declared():
+        if n not in ("moe_status_string", "moe_last_error_detail") and not n.endswith("_workspace_bytes"):
+            assert hasattr(moe, n), n
+
+
+def _status(lib, fn, *args):
+    f = getattr(lib, fn)
+    f.restype = ctypes.c_int
+    return f(*args)
+
+
+def test_host_validation_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)          # never dereferenced: validation fails first
+    odd = P(0x1002)           # misaligned
+    null = None
+    lib.moe_last_error_detail.restype = ctypes.c_char_p
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
+    # route: k > E, E too large, H not a multiple of 128, null pointers, small workspace
+    assert _status(lib, "moe_route", fake, fake, fake, 4, 256, 8, 9, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -2
+    assert _status(lib, "moe_route", fake, fake, fake, 4, 256, 2000, 8, 1, fake, fake, fake, ctypes.c_size_t(1 << 30), null) == -2
+    assert _status(lib, "moe_route", fake, fake, fake, 4, 200, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -2
+    assert _status(lib, "moe_route", null, fake, fake, 4, 256, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -1
+    assert _status(lib, "moe_route", odd, fake, fake, 4, 256, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -1
+    assert _status(lib, "moe_route", fake, fake, fake, 4, 256, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(8), null) == -3
+    assert b"workspace" in lib.moe_last_error_detail()
+    assert lib.moe_route_workspace_bytes(64, 384) == 64 * 384 * 4
+    # zero tokens is a no-op
+    assert _status(lib, "moe_route", null, null, null, 0, 256, 16, 2, 1, null, null, null, ctypes.c_size_t(0), null) == 0
+    # permute: E too large, k > 16
+    assert _status(lib, "moe_permute", fake, 4, 2, 4096, fake, fake, fake, fake, null) == -2
+    assert _status(lib, "moe_permute", fake, 4, 17, 64, fake, fake, fake, fake, null) == -2
+    assert _status(lib, "moe_permute", fake, 4, 2, 64, null, fake, fake, fake, null) == -1
+    # grouped gemms: bad mode, unsupported widths, scales in the wrong mode, null pointers
+    g = "moe_int4_grouped_swiglu"
+    assert _status(lib, g, 7, fake, null, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
+    assert _status(lib, g, 0, fake, null, fake, fake, fake, fake, fake, fake, 4, 2, 16, 200, 128, fake, null, null) == -2
+    assert _status(lib, g, 0, fake, null, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 96, fake, null, null) == -2
+    assert _status(lib, g, 0, fake, fake, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
+    assert _status(lib, g, 1, fake, null, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
+    assert _status(lib, g, 0, fake, null, null, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
+    d = "moe_int4_grouped_down"
+    assert _status(lib, d, 0, fake, null, fake, fake, fake, 4, 2, 16, 128, 384, fake, null) == -2
+    assert _status(lib, d, 1, fake, null, fake, fake, fake, 4, 2, 16, 128, 256, fake, null) == -1
+    # combine: exact mode with a shared input, misaligned output
+    assert _status(lib, "moe_combine", 1, fake, fake, fake, fake, 4, 2, 256, fake, null) == -1
+    assert _status(lib, "moe_combine", 0, fake, fake, fake, null, 4, 2, 256, odd, null) == -1
+    # dense: N not a multiple of 64, K not a multiple of 128
+    assert _status(lib, "moe_linear_bf16", fake, fake, null, fake, 4, 100, 256, null, ctypes.c_size_t(0), null) == -2
+    assert _status(lib, "moe_linear_bf16", fake, fake, null, fake, 4, 128, 200, null, ctypes.c_size_t(0), null) == -2
+    lib.moe_dense_workspace_bytes.restype = ctypes.c_size_t
+    need = lib.moe_dense_workspace_bytes(64, 4096, 7168)
+    assert need > 0  # decode shapes split K
+    assert _status(lib, "moe_dense_swiglu_bf16", fake, fake, fake, fake, 64, 7168, 2048, null, ctypes.c_size_t(0), null) == -3
+    assert lib.moe_dense_workspace_bytes(8192, 4096, 7168) == 0
+    assert _status(lib, "moe_rmsnorm_bf16", fake, fake, ctypes.c_float(-1.0), fake, 4, 64, null) == -1
+    assert _status(lib, "moe_int4_group_sums_i32", fake, fake, 20, 16, 64, fake, null) == -2
+    assert lib.moe_status_string(-3) == b"workspace missing or too small"

@@ -1,0 +1,308 @@
+"""Per-kernel parity of the HIP path against the oracle, through the C ABI, on
+seeded inputs that span several tiles and a ragged tail (GPU required)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import refmath
+from tests.gpu_common import (assert_bf16_close, assert_f32_close, bf16_dev, np_bf16, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from int4_routed_expert_moe_amd import moe
+    return moe
+
+
+def _rand_bf16(g, shape, std=1.0):
+    return refmath.bf16_from_f32((g.standard_normal(shape) * std).astype(np.float32))
+
+
+def _packed(g, shape):
+    return g.integers(0, 256, shape, dtype=np.uint8)
+
+
+def _scales(g, shape):
+    return refmath.bf16_from_f32(g.uniform(0.005, 0.02, shape).astype(np.float32))
+
+
+# ---------------------------------------------------------------- routing
+@pytest.mark.parametrize("T,H,E,k,seed", [
+    (1, 128, 16, 1, 0), (37, 256, 16, 2, 1), (64, 7168, 384, 8, 2), (300, 1024, 384, 8, 3),
+    (130, 512, 1000, 16, 4), (64, 256, 8, 8, 5),
+])
+def test_route_bitexact(m, T, H, E, k, seed):
+    say(f"route T={T} H={H} E={E} k={k}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (T, H))
+    w = _rand_bf16(g, (E, H), 0.02)
+    b = g.uniform(-0.1, 0.1, E).astype(np.float32)
+    if E >= 8:  # exact ties: duplicated router rows with equal bias
+        w[3] = w[1]
+        w[5] = w[1]
+        b[3] = b[1]
+        b[5] = b[1]
+    ridx, rw = oracle.route(x, w, b, k, True)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.moe_route_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
+    m.moe_route(bf16_dev(x), bf16_dev(w), torch.from_numpy(b).cuda(), k, True, idx, wt, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_array_equal(wt.cpu().numpy(), rw)
+    # renormalisation off
+    ridx2, rw2 = oracle.route(x, w, b, k, False)
+    m.moe_route(bf16_dev(x), bf16_dev(w), torch.from_numpy(b).cuda(), k, False, idx, wt, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx2)
+    np.testing.assert_array_equal(wt.cpu().numpy(), rw2)
+
+
+def test_sigmoid_matches_oracle_on_a_sweep(m):
+    """Route with one expert row per logit value: the selected weight (renormalise
+    off, k=E) is the sigmoid of that logit, bit for bit."""
+    say("sigmoid sweep")
+    H, E = 128, 64
+    vals = np.linspace(-90, 90, 64 * 97, dtype=np.float32)
+    # logit = x[0] * w[e,0] with x = (1, 0, ...): w[e,0] carries the value (bf16-rounded)
+    wv = refmath.bf16_from_f32(vals)
+    T = 1
+    for c in range(0, len(wv), E):
+        w = np.zeros((E, H), np.uint16)
+        w[:, 0] = wv[c:c + E]
+        x = np.zeros((T, H), np.uint16)
+        x[0, 0] = 0x3F80
+        b = np.zeros(E, np.float32)
+        ridx, rw = oracle.route(x, w, b, E, False)
+        idx = torch.empty((T, E), dtype=torch.int32, device="cuda")
+        wt = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        ws = torch.empty(m.moe_route_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
+        m.moe_route(bf16_dev(x), bf16_dev(w), torch.from_numpy(b).cuda(), E, False, idx, wt, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+        np.testing.assert_array_equal(wt.cpu().numpy(), rw)
+
+
+# ---------------------------------------------------------------- permutation
+@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (64, 2, 16, 1), (64, 8, 384, 2), (8192, 8, 384, 3),
+                                        (1000, 16, 1024, 4), (77, 3, 5, 5)])
+def test_permute_bitexact(m, T, k, E, seed):
+    say(f"permute T={T} k={k} E={E}")
+    g = np.random.default_rng(seed)
+    idx = g.integers(0, E, (T, k)).astype(np.int32)
+    if E > 4:
+        idx[idx == 2] = 3  # an empty expert
+    rc, ro, rs, rp = oracle.permute(idx, E)
+    S = T * k
+    d = {n: torch.empty(s, dtype=torch.int32, device="cuda") for n, s in
+         (("counts", E), ("offsets", E + 1), ("ss", S), ("sp", S))}
+    m.moe_permute(torch.from_numpy(idx).cuda(), E, d["counts"], d["offsets"], d["ss"], d["sp"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d["counts"].cpu().numpy(), rc)
+    np.testing.assert_array_equal(d["offsets"].cpu().numpy(), ro)
+    np.testing.assert_array_equal(d["ss"].cpu().numpy(), rs)
+    np.testing.assert_array_equal(d["sp"].cpu().numpy(), rp)
+
+
+# ---------------------------------------------------------------- exact-mode primitives
+@pytest.mark.parametrize("M,K,seed", [(1, 32, 0), (37, 256, 1), (64, 7168, 2)])
+def test_quant_act_bitexact(m, M, K, seed):
+    say(f"quant M={M} K={K}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (M, K))
+    x[0, :32] = 0  # a zero group
+    if K >= 64:
+        x[0, 32:64] = refmath.bf16_from_f32(np.array([127.0, 2.5, -2.5, 3.5] + [0.0] * 28, np.float32))
+    rq, rs = oracle.quant_act_int8(x)
+    q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    s = torch.empty((M, K // 32), dtype=torch.float32, device="cuda")
+    m.moe_quant_act_int8(bf16_dev(x), q, s)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(16, 16, 32, 0), (48, 32, 7168, 1), (16, 64, 2048, 2)])
+def test_group_sums_bitexact(m, M, N, K, seed):
+    say(f"group sums M={M} N={N} K={K}")
+    g = np.random.default_rng(seed)
+    qx = g.integers(-127, 128, (M, K)).astype(np.int8)
+    qx[0, :32] = 127
+    packed = _packed(g, (N, K // 2))
+    packed[0, :16] = 0x88
+    ref = oracle.group_sums(qx, packed, K)
+    G = torch.empty((M, N, K // 32), dtype=torch.int32, device="cuda")
+    m.moe_int4_group_sums_i32(torch.from_numpy(qx).cuda(), torch.from_numpy(packed).cuda(), G)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(G.cpu().numpy(), ref)
+    assert int(G[0, 0, 0]) == -32512
+
+
+# ---------------------------------------------------------------- grouped expert GEMMs
+def _expert_set(g, E, H, I):
+    return {"wg": _packed(g, (E, I, H // 2)), "sg": _scales(g, (E, I, H // 32)),
+            "wu": _packed(g, (E, I, H // 2)), "su": _scales(g, (E, I, H // 32)),
+            "wd": _packed(g, (E, H, I // 2)), "sd": _scales(g, (E, H, I // 32))}
+
+
+def _dev_experts(W):
+    out = {}
+    for n in ("wg", "wu", "wd"):
+        out[n] = torch.from_numpy(W[n]).cuda()
+    for n in ("sg", "su", "sd"):
+        out[n] = bf16_dev(W[n])
+    return out
+
+
+def _routing(g, T, E, k, skew=False):
+    if skew:  # heavy head + empty experts
+        p = np.arange(1, E + 1, dtype=np.float64) ** -1.5
+        p[E // 2:] = 0
+        p /= p.sum()
+    else:
+        p = np.full(E, 1.0 / E)
+    idx = np.stack([g.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    w = g.uniform(0.05, 0.3, (T, k)).astype(np.float32)
+    return idx, w
+
+
+@pytest.mark.parametrize("T,H,I,E,k,skew,seed", [
+    (64, 256, 128, 16, 2, False, 0),     # tiny workload shape
+    (37, 512, 256, 8, 3, False, 1),      # ragged tail, one tile per expert
+    (300, 256, 128, 4, 2, True, 2),      # many rows per expert (several tiles) and empty experts
+    (700, 384, 256, 6, 2, False, 3),     # largest tile height
+])
+def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
+    say(f"grouped bf16 T={T} H={H} I={I} E={E} k={k}")
+    g = np.random.default_rng(seed)
+    W = _expert_set(g, E, H, I)
+    x = _rand_bf16(g, (T, H))
+    idx, w = _routing(g, T, E, k, skew)
+    counts, offsets, ss, sp = oracle.permute(idx, E)
+    S = T * k
+    rows = x[ss // k]
+    ref = oracle.experts_bf16(rows, idx.reshape(-1)[ss], W, want=("h", "y"))
+    D = _dev_experts(W)
+    off_d = torch.from_numpy(offsets).cuda()
+    h = torch.empty((S, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((S, H), dtype=torch.bfloat16, device="cuda")
+    m.moe_int4_grouped_swiglu(m.MOE_MODE_BF16, bf16_dev(x), None, D["wg"], D["sg"], D["wu"], D["su"], off_d,
+                              torch.from_numpy(ss).cuda(), T, k, E, H, I, h, None)
+    # down on the oracle's h so the two stages are checked separately
+    m.moe_int4_grouped_down(m.MOE_MODE_BF16, bf16_dev(ref["h"]), None, D["wd"], D["sd"], off_d, T, k, E, I, H, y)
+    torch.cuda.synchronize()
+    assert_bf16_close(np_bf16(h), ref["h"], "h")
+    assert_bf16_close(np_bf16(y), ref["y"], "y")
+    # combine on the GPU's y vs the oracle combine of the same y
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    shared = _rand_bf16(g, (T, H))
+    m.moe_combine(m.MOE_MODE_BF16, y, torch.from_numpy(sp).cuda(), torch.from_numpy(w).cuda(), bf16_dev(shared),
+                  T, k, H, out)
+    torch.cuda.synchronize()
+    y_np = np_bf16(y)
+    ref_out = oracle.combine_bf16(y_np[sp].reshape(T, k, H), w, shared)
+    assert_bf16_close(np_bf16(out), ref_out, "combine", atol_rms=1e-3, rtol=8e-3)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,skew,seed", [
+    (64, 256, 128, 16, 2, False, 0),
+    (300, 256, 128, 4, 2, True, 1),
+    (45, 512, 256, 5, 3, False, 2),
+])
+def test_grouped_exact_bitexact(m, T, H, I, E, k, skew, seed):
+    say(f"grouped exact T={T} H={H} I={I} E={E} k={k}")
+    g = np.random.default_rng(seed)
+    W = _expert_set(g, E, H, I)
+    x = _rand_bf16(g, (T, H))
+    idx, w = _routing(g, T, E, k, skew)
+    counts, offsets, ss, sp = oracle.permute(idx, E)
+    S = T * k
+    qx, sx = oracle.quant_act_int8(x)
+    ref = oracle.experts_exact(qx[ss // k], sx[ss // k], idx.reshape(-1)[ss], W, want=("g", "u", "qh", "sh", "y"))
+    D = _dev_experts(W)
+    off_d = torch.from_numpy(offsets).cuda()
+    qh = torch.empty((S, I), dtype=torch.int8, device="cuda")
+    sh = torch.empty((S, I // 32), dtype=torch.float32, device="cuda")
+    y = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    m.moe_int4_grouped_swiglu(m.MOE_MODE_EXACT_I8, torch.from_numpy(qx).cuda(), torch.from_numpy(sx).cuda(),
+                              D["wg"], D["sg"], D["wu"], D["su"], off_d, torch.from_numpy(ss).cuda(), T, k, E, H, I,
+                              qh, sh)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sh.cpu().numpy(), ref["sh"])
+    np.testing.assert_array_equal(qh.cpu().numpy(), ref["qh"])
+    m.moe_int4_grouped_down(m.MOE_MODE_EXACT_I8, qh, sh, D["wd"], D["sd"], off_d, T, k, E, I, H, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), ref["y"])
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    m.moe_combine(m.MOE_MODE_EXACT_I8, y, torch.from_numpy(sp).cuda(), torch.from_numpy(w).cuda(), None, T, k, H, out)
+    torch.cuda.synchronize()
+    ref_out = oracle.combine_f32(ref["y"][sp].reshape(T, k, H), w)
+    np.testing.assert_array_equal(out.cpu().numpy(), ref_out)
+
+
+# ---------------------------------------------------------------- dense pieces
+@pytest.mark.parametrize("M,N,K,with_add,seed", [
+    (1, 64, 128, False, 0), (64, 2048, 7168, False, 1), (40, 192, 512, True, 2), (200, 256, 384, True, 3),
+    (700, 512, 256, False, 4),
+])
+def test_linear_bf16(m, M, N, K, with_add, seed):
+    say(f"linear M={M} N={N} K={K}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (M, K))
+    w = _rand_bf16(g, (N, K), 1.0 / np.sqrt(K))
+    add = _rand_bf16(g, (M, N)) if with_add else None
+    ref = oracle.linear_bf16(x, w, add)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    nb = m.moe_dense_workspace_bytes(M, N, K)
+    ws = torch.empty(max(1, nb), dtype=torch.uint8, device="cuda")
+    m.moe_linear_bf16(bf16_dev(x), bf16_dev(w), None if add is None else bf16_dev(add), y, ws)
+    torch.cuda.synchronize()
+    assert_bf16_close(np_bf16(y), ref, "linear")
+
+
+@pytest.mark.parametrize("M,H,I,seed", [(64, 256, 128, 0), (64, 7168, 2048, 1), (130, 512, 192, 2)])
+def test_dense_swiglu_and_silu_mul(m, M, H, I, seed):
+    say(f"dense swiglu M={M} H={H} I={I}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (M, H))
+    wg = _rand_bf16(g, (I, H), 1.0 / np.sqrt(H))
+    wu = _rand_bf16(g, (I, H), 1.0 / np.sqrt(H))
+    wd = _rand_bf16(g, (H, I), 1.0 / np.sqrt(I))
+    ref_h, _ = oracle.dense_swiglu_bf16(x, wg, wu, wd, want_h=True)
+    h = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(1, m.moe_dense_workspace_bytes(M, 2 * I, H)), dtype=torch.uint8, device="cuda")
+    m.moe_dense_swiglu_bf16(bf16_dev(x), bf16_dev(wg), bf16_dev(wu), h, ws)
+    torch.cuda.synchronize()
+    assert_bf16_close(np_bf16(h), ref_h, "dense swiglu h")
+    # elementwise silu*mul against the oracle's rounding chain on given g, u
+    gg = _rand_bf16(g, (M, I), 3.0)
+    uu = _rand_bf16(g, (M, I), 3.0)
+    hh = torch.empty((M, I), dtype=torch.bfloat16, device="cuda")
+    m.moe_silu_mul_bf16(bf16_dev(gg), bf16_dev(uu), hh)
+    torch.cuda.synchronize()
+    a = refmath.bf16_from_f64(refmath.silu64(refmath.bf16_to_f32(gg)))
+    ref = refmath.bf16_from_f64(refmath.bf16_to_f32(a).astype(np.float64) * refmath.bf16_to_f32(uu))
+    diff = np.abs(np_bf16(hh).astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1 and (diff > 0).mean() < 0.01
+
+
+@pytest.mark.parametrize("M,N,seed", [(1, 3584, 0), (70, 3584, 1), (5, 256, 2)])
+def test_rmsnorm(m, M, N, seed):
+    say(f"rmsnorm M={M} N={N}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (M, N), 2.0)
+    x[0] = refmath.bf16_from_f32(np.full(N, 0.75, np.float32))
+    gain = refmath.bf16_from_f32(g.uniform(0.9, 1.1, N).astype(np.float32))
+    ref = oracle.rmsnorm_bf16(x, gain, 1e-6)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    m.moe_rmsnorm_bf16(bf16_dev(x), bf16_dev(gain), 1e-6, y)
+    torch.cuda.synchronize()
+    got = np_bf16(y)
+    diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1, "rmsnorm differs by more than one bf16 step"
+    np.testing.assert_array_equal(got[0], ref[0])

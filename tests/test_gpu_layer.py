@@ -1,0 +1,109 @@
+"""End-to-end parity of the whole layer (route -> permute -> experts -> combine,
++ shared expert, + latent wrapper, + exact mode) on the five workloads, at
+their full sizes, in the launch configuration the benchmark times.
+
+Routing and the permutation are compared on every token; expert outputs on
+all tokens where the oracle finishes in seconds, otherwise on a seeded token
+sample (the layer is token-independent after routing)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int4_routed_expert_moe_amd import synthetic
+from tests.gpu_common import (assert_bf16_close, assert_f32_close, bf16_dev, inputs, layer, np_bf16, say)
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = {1: None, 2: None, 3: 24, 4: 16, 5: 24}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(cfg_id):
+    inp = inputs(cfg_id)
+    L = layer(cfg_id)
+    x = bf16_dev(inp["x"])
+    say(f"layer forward workload {cfg_id} ({inp['cfg']['name']}) T={inp['cfg']['T']}")
+    out = L.forward(x)
+    torch.cuda.synchronize()
+    return inp, L, x, out
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 5, 3, 4])
+def test_layer_parity(cfg_id):
+    inp, L, x, out = _run(cfg_id)
+    cfg = inp["cfg"]
+    T, k, E = cfg["T"], cfg["k"], cfg["E"]
+    ws = L.workspace(T)
+    # routing: bit-exact on every token
+    ridx, rw = oracle.route(inp["x"], inp["router_w"], inp["router_b"], k, True)
+    np.testing.assert_array_equal(ws["topk_idx"].cpu().numpy(), ridx)
+    np.testing.assert_array_equal(ws["topk_w"].cpu().numpy(), rw)
+    # permutation: bit-exact
+    rc, ro, rs, rp = oracle.permute(ridx, E)
+    np.testing.assert_array_equal(ws["counts"].cpu().numpy(), rc)
+    np.testing.assert_array_equal(ws["offsets"].cpu().numpy(), ro)
+    np.testing.assert_array_equal(ws["sorted_slot"].cpu().numpy(), rs)
+    np.testing.assert_array_equal(ws["slot_pos"].cpu().numpy(), rp)
+    if cfg.get("zipf"):
+        dead = inp["router_b"] == np.float32(-4.0)
+        assert rc[dead].sum() == 0 and dead.sum() == round(0.2 * E)
+    # outputs on all tokens or a sample
+    n = SAMPLE[cfg_id]
+    toks = np.arange(T) if n is None else synthetic.token_sample(cfg, n)
+    say(f"oracle on {len(toks)} tokens of workload {cfg_id}")
+    ref, inter = oracle.layer_tokens(inp, toks, topk_idx=ridx, topk_w=rw, want_intermediates=True)
+    slots = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    pos = rp[slots]
+    if cfg["mode"] == "exact":
+        np.testing.assert_array_equal(ws["qx"].cpu().numpy()[toks], inter["qx"])
+        np.testing.assert_array_equal(ws["sx"].cpu().numpy()[toks], inter["sx"])
+        np.testing.assert_array_equal(ws["h_scale"].cpu().numpy()[pos], inter["sh"])
+        np.testing.assert_array_equal(ws["h"].cpu().numpy()[pos], inter["qh"])
+        np.testing.assert_array_equal(ws["y"].cpu().numpy()[pos], inter["y"])
+        got = out.cpu().numpy()[toks]
+        assert_f32_close(got, ref, "exact out", 1e-5)
+        np.testing.assert_array_equal(got, ref)
+    else:
+        assert_bf16_close(np_bf16(ws["h"])[pos], inter["h"], "h")
+        if cfg.get("L"):
+            assert_bf16_close(np_bf16(ws["x_lat"])[toks], inter["x_lat"], "x_lat")
+            assert_bf16_close(np_bf16(ws["routed"])[toks], inter["routed"], "routed")
+        if inp.get("shared") is not None:
+            assert_bf16_close(np_bf16(ws["shared_out"])[toks], inter["shared"], "shared")
+        worst = assert_bf16_close(np_bf16(out)[toks], ref, "out")
+        say(f"workload {cfg_id}: worst |err|/rms = {worst:.3g}")
+
+
+@pytest.mark.parametrize("cfg_id", [2, 4])
+def test_layer_deterministic(cfg_id):
+    inp, L, x, out = _run(cfg_id)
+    a = out.clone()
+    ws = L.workspace(inp["cfg"]["T"])
+    h1 = ws["h"].clone()
+    out2 = L.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                       out2.view(torch.int32) if out2.dtype == torch.float32 else out2.view(torch.int16))
+    assert torch.equal(h1, ws["h"])
+
+
+def test_layer_edge_token_counts():
+    """T = 1 and a ragged T on the tiny layer; every row checked against the oracle."""
+    inp = inputs(1)
+    L = layer(1)
+    for T in (1, 7, 50):
+        say(f"tiny layer T={T}")
+        x = inp["x"][:T]
+        out = L.forward(bf16_dev(x))
+        torch.cuda.synchronize()
+        ref = oracle.layer_tokens(dict(inp, x=x), np.arange(T))
+        assert_bf16_close(np_bf16(out), ref, f"T={T}")
+    # empty input is a no-op
+    out = L.forward(bf16_dev(inp["x"][:0]))
+    assert out.shape[0] == 0
