@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--kernel-steps", type=int, default=10, help="forwards timed per kernel with events")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device-to-device copy of this many MiB (3 times), the reference "
+                         "kernel for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -122,6 +125,14 @@ def main():
     t_gen = time.perf_counter() - t_gen
     T = cfg["T"]
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         layer.forward(x)
     torch.cuda.synchronize()

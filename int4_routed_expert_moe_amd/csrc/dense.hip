@@ -107,9 +107,9 @@ __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
         for (int it = 0; it < A_ITERS; ++it) {
             const int lin = it * 256 + tid;
             const int row = lin >> 4, piece = lin & 15;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (row < rows) v = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)(m0 + row) * K + c * kDKC + piece * 8);
-            Aq[it] = v;
+            // rows past the tile load the tile's first row and are zeroed by a select
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)(m0 + (row < rows ? row : 0)) * K + c * kDKC + piece * 8);
+            Aq[it] = row < rows ? v : u32x4_t{0u, 0u, 0u, 0u};
         }
     };
     auto store_A = [&]() {

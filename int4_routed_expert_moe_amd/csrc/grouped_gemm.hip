@@ -249,25 +249,20 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
             const int lin = it * 256 + tid;
             const int row = lin / PIECES;
             const int piece = lin % PIECES;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (row < BM) {
-                const int src = rowsrc[row];
-                if (src >= 0) {
-                    if (!EXACT) {
-                        const uint16_t* p = static_cast<const uint16_t*>(a.act) + (size_t)src * K + c * kKC + piece * 8;
-                        v = *reinterpret_cast<const u32x4_t*>(p);
-                    } else {
-                        const int8_t* p = static_cast<const int8_t*>(a.act) + (size_t)src * K + c * kKC + piece * 16;
-                        v = *reinterpret_cast<const u32x4_t*>(p);
-                    }
-                }
-            }
-            Aq[it] = v;
+            // rows past the tile load row 0 and are zeroed by a select (no load under a branch)
+            const int src = rowsrc[row < BM ? row : 0];
+            const int srow = (row < BM && src >= 0) ? src : 0;
+            u32x4_t v;
+            if (!EXACT)
+                v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + (size_t)srow * K + c * kKC + piece * 8);
+            else
+                v = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + (size_t)srow * K + c * kKC + piece * 16);
+            Aq[it] = (row < BM && src >= 0) ? v : u32x4_t{0u, 0u, 0u, 0u};
         }
-        if (EXACT && tid < BM) {
-            const int src = rowsrc[tid];
-            SXq = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (src >= 0) SXq = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)src * (K / 32) + c * 4);
+        if (EXACT) {
+            const int src = rowsrc[tid < BM ? tid : 0];
+            const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)max(src, 0) * (K / 32) + c * 4);
+            SXq = (tid < BM && src >= 0) ? sv : f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     };
     auto store_A = [&]() {
@@ -423,6 +418,265 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     }
 }
 
+// Tiles of at most 16 rows (decode): the weights dominate the bytes, so each
+// wave streams its 64 weight rows independently with no workgroup barrier,
+// keeping the loads of the next two 128-wide K chunks in flight while it
+// converts and multiplies the current one.  The tile's activation rows (rows
+// past the tile's count read as zero) come straight from L2 in the MFMA
+// operand layout.
+//
+// Scales are staged in wave-private LDS per 1024-wide K block (32 scales = 64
+// bytes per row): each chunk also loads one eighth of the NEXT block's scale
+// rows as whole 64-byte segments, written to the other LDS buffer right after
+// the chunk is consumed.  Reading 2-8 scale bytes per row per chunk instead
+// would refetch each scale line from HBM many times (the scale rows of all
+// waves in flight outgrow the L2).  Every chunk issues the same unconditional
+// loads, so the outstanding-load counts stay exact.  Same arithmetic as k_grouped.
+constexpr int kSBlk = 8;        // chunks per scale block (32 scales per row)
+constexpr int kSStride = 36;    // halves per LDS scale row (32 + 4 pad)
+
+template <int MODE, int OP>
+__global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
+    constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
+    constexpr bool GATEUP = OP == 0;
+    __shared__ __attribute__((aligned(16))) uint16_t Ssm[4][2][64][kSStride];
+
+    const long L = xcd_logical_block(a.per_xcd);
+    if (L >= a.n_logical) return;
+    const long tile = L / a.n_chunks;
+    const int nc = (int)(L % a.n_chunks);
+    TileInfo ti;
+    if (!find_tile(a.offsets, a.E, 16, tile, ti)) return;
+
+    const int lane = lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int r = lane & 15;
+    const int j = lane >> 4;
+    const int K = a.K;
+    const int N = a.N;
+    const int nch = K / kKC;
+    const int srow_len = K / 32;  // scales per weight row (a multiple of 4)
+
+    auto src_of = [&](int row) -> int {
+        if (row >= ti.rows) return -1;
+        return GATEUP ? a.sorted_slot[ti.row0 + row] / a.k : ti.row0 + row;
+    };
+    const int asrc = src_of(r);
+    const bool avalid = asrc >= 0;
+    const int arow = avalid ? asrc : 0;
+    int dsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dsrc[i] = EXACT ? src_of(4 * j + i) : -1;
+
+    // weight row of wave-local row index q (0..63): column block q/16, row q%16
+    const size_t wmat = (size_t)N * (size_t)(K / 2);
+    const size_t smat = (size_t)N * (size_t)(K / 32);
+    const int n0 = GATEUP ? nc * 128 + wave * 32 : nc * 256 + wave * 64;
+    auto wrow_of = [&](int q) -> size_t {  // row index within its matrix
+        return GATEUP ? (size_t)(n0 + 16 * ((q >> 4) & 1) + (q & 15)) : (size_t)(n0 + q);
+    };
+    auto mat_of = [&](int q) -> int { return GATEUP ? (q >> 5) : 0; };  // 0 = w0/s0, 1 = w1/s1
+    const uint8_t* wrow[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const int q = 16 * cb + r;
+        wrow[cb] = (mat_of(q) ? a.w1 : a.w0) + (size_t)ti.e * wmat + wrow_of(q) * (K / 2);
+    }
+    // scale rows this lane stages: row 8*(c%8) + lane/8 of the wave's 64, 8 bytes at (lane%8)*8
+    auto srow_ptr = [&](int q) -> const uint16_t* {
+        return (mat_of(q) ? a.s1 : a.s0) + (size_t)ti.e * smat + wrow_of(q) * srow_len;
+    };
+
+    struct Chunk {
+        u32x4_t B[4];     // bf16 mode: one scale group per column block; exact: dwords of groups 0..3
+        u32x4_t A[4];     // bf16: 8 bf16 per MFMA step; exact: 8 int8 per group in A[g][0..1]
+        f32x4_t SX[4];    // exact: s_x of result rows 4j+i for groups 0..3
+        u32x2_t SN;       // 4 scales of the next scale block (one piece of one row)
+    };
+    auto load = [&](int c, Chunk& ch) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            if (!EXACT) {
+                ch.B[cb] = *reinterpret_cast<const u32x4_t*>(wrow[cb] + (size_t)c * 64 + 16 * j);
+            } else {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    ch.B[cb][g] = *reinterpret_cast<const uint32_t*>(wrow[cb] + (size_t)c * 64 + 16 * g + 4 * j);
+            }
+        }
+        // rows past the tile read row 0 (zeroed at use): no load sits under a branch
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x4_t v;
+            if (!EXACT) {
+                v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + (size_t)arow * K +
+                                                       c * kKC + 32 * j + 8 * g);
+            } else {
+                const u32x2_t q = *reinterpret_cast<const u32x2_t*>(static_cast<const int8_t*>(a.act) +
+                                                                     (size_t)arow * K + c * kKC + 32 * g + 8 * j);
+                v = u32x4_t{q[0], q[1], 0u, 0u};
+            }
+            ch.A[g] = v;
+        }
+        if (EXACT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ch.SX[i] = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)max(dsrc[i], 0) * (K / 32) + c * 4);
+        }
+        // next block's scales: row 8*(c%8) + lane/8, scales [32*(c/8+1) + 4*(lane%8), +4)
+        const int q = 8 * (c % kSBlk) + (lane >> 3);
+        const int sidx = 32 * (c / kSBlk + 1) + 4 * (lane & 7);
+        const int sclamp = sidx < srow_len ? sidx : 0;  // past the row: a valid address, never used
+        ch.SN = *reinterpret_cast<const u32x2_t*>(srow_ptr(q) + sclamp);
+    };
+    auto stage_next = [&](int c, const Chunk& ch) {  // after chunk c is consumed
+        const int q = 8 * (c % kSBlk) + (lane >> 3);
+        *reinterpret_cast<u32x2_t*>(&Ssm[wave][(c / kSBlk + 1) & 1][q][4 * (lane & 7)]) = ch.SN;
+    };
+
+    f32x4_t acc[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int c, const Chunk& ch) {
+        const uint16_t(*sb)[kSStride] = Ssm[wave][(c / kSBlk) & 1];
+        const int cl = c % kSBlk;
+        if (!EXACT) {
+            half2_t s2[4], c2[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) scale_pair(sb[16 * cb + r][4 * cl + j], s2[cb], c2[cb]);
+#pragma unroll
+            for (int gp = 0; gp < 4; ++gp) {
+                const u32x4_t av = avalid ? ch.A[gp] : u32x4_t{0u, 0u, 0u, 0u};
+                const half8_t af = __builtin_bit_cast(half8_t, bf16x8_to_f16_perm(av));
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, dequant8(ch.B[cb][gp], s2[cb], c2[cb]),
+                                                                    acc[cb], 0, 0, 0);
+            }
+        } else {
+            u32x2_t sv[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) sv[cb] = *reinterpret_cast<const u32x2_t*>(&sb[16 * cb + r][4 * cl]);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const u32x4_t a16 = i8x8_to_f16_perm(avalid ? ch.A[g][0] : 0u, avalid ? ch.A[g][1] : 0u);
+                const half8_t af = __builtin_bit_cast(half8_t, a16);
+                f32x4_t sx;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sx[i] = dsrc[i] >= 0 ? ch.SX[i][g] : 0.0f;
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    half2_t s2, c2;
+                    scale_pair(sv[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
+                    const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        af, dequant8(ch.B[cb][g], s2, c2), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[cb][i] = __builtin_fmaf(d[i], sx[i], acc[cb][i]);
+                }
+            }
+        }
+    };
+
+    // prologue: scale block 0 of all 64 rows, 8-byte pieces (4 scales; a row holds a
+    // multiple of 4 scales, so a piece lies wholly inside or wholly past its row)
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int q = 8 * it + (lane >> 3);
+        const int sidx = 4 * (lane & 7);
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(srow_ptr(q) + (sidx < srow_len ? sidx : 0));
+        *reinterpret_cast<u32x2_t*>(&Ssm[wave][0][q][sidx]) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    // Three chunk slots: the two ahead are in flight while one is consumed.
+    // Chunk indices past the end are clamped (a redundant in-bounds load) rather
+    // than skipped, so no load sits under a branch; the scheduling barriers keep
+    // each chunk's loads where they are issued.
+    Chunk c0, c1, c2;
+    load(0, c0);
+    load(min(1, nch - 1), c1);
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](int c, Chunk& cur, int cnext) {
+        compute(c, cur);
+        stage_next(c, cur);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        load(min(cnext, nch - 1), cur);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int c = 0;
+    for (; c + 3 <= nch; c += 3) {
+        load(min(c + 2, nch - 1), c2);
+        __builtin_amdgcn_sched_barrier(0);
+        step(c, c0, c + 3);
+        step(c + 1, c1, c + 4);
+        compute(c + 2, c2);
+        stage_next(c + 2, c2);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (c < nch) {
+        compute(c, c0);
+        stage_next(c, c0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (c + 1 < nch) compute(c + 1, c1);
+
+    // epilogue (rows 4j+i of the lane)
+    if (GATEUP) {
+        const int grp = n0 / 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rl = 4 * j + i;
+            const bool ok = rl < ti.rows;
+            const size_t orow = (size_t)(ti.row0 + rl);
+            if (!EXACT) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const uint32_t gb = f32_to_bf16_bits(acc[p][i]);
+                    const uint32_t ub = f32_to_bf16_bits(acc[2 + p][i]);
+                    const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
+                    const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
+                    if (ok) static_cast<uint16_t*>(a.out)[orow * N + n0 + 16 * p + r] = (uint16_t)hb;
+                }
+            } else {
+                const float h0 = moe_silu(acc[0][i]) * acc[2][i];
+                const float h1 = moe_silu(acc[1][i]) * acc[3][i];
+                float amax = fmaxf(fabsf(h0), fabsf(h1));
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+                const float s = (amax == 0.0f) ? 0.0f : amax / 127.0f;
+                if (ok) {
+                    int8_t* o = static_cast<int8_t*>(a.out) + orow * N + n0 + r;
+                    o[0] = (int8_t)moe_quant_i8(h0, s);
+                    o[16] = (int8_t)moe_quant_i8(h1, s);
+                    if (r == 0) a.out_scale[orow * (N / 32) + grp] = s;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rl = 4 * j + i;
+            if (rl >= ti.rows) continue;
+            const size_t orow = (size_t)(ti.row0 + rl);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int col = n0 + 16 * cb + r;
+                if (!EXACT)
+                    static_cast<uint16_t*>(a.out)[orow * N + col] = (uint16_t)f32_to_bf16_bits(acc[cb][i]);
+                else
+                    static_cast<float*>(a.out)[orow * N + col] = acc[cb][i];
+            }
+        }
+    }
+}
+
 // Rows per tile: as many 16-row blocks as an average expert segment needs.
 int pick_mb(int S, int E) {
     const double avg = (double)S / (double)E;
@@ -441,7 +695,7 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
     a.per_xcd = moe::per_xcd(a.n_logical);
     const dim3 grid(8 * a.per_xcd), block(256);
     switch (mb) {
-    case 1: hipLaunchKernelGGL((k_grouped<MODE, OP, 1>), grid, block, 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_grouped_skinny<MODE, OP>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((k_grouped<MODE, OP, 2>), grid, block, 0, st, a); break;
     case 4: hipLaunchKernelGGL((k_grouped<MODE, OP, 4>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((k_grouped<MODE, OP, 8>), grid, block, 0, st, a); break;

@@ -9,71 +9,122 @@
 // one fp32 chain summed in ascending hidden index from 0 (no split, no
 // matrix cores: their internal summation order is unspecified).  Lanes are
 // tokens and each wave runs EPW such chains (one per expert) side by side;
-// the expert rows are wave-uniform, so they come through the scalar cache.
+// the expert rows are wave-uniform LDS reads (broadcasts).
 #include "moe_common.h"
 
 namespace {
 
 constexpr int kRouteTok = 64;   // tokens per block (one per lane)
-constexpr int kRouteKC = 128;   // hidden elements staged per LDS chunk
+constexpr int kRouteKC = 64;    // hidden elements staged per LDS chunk
 constexpr int kRouteWaves = 4;
 
+// Logits of 64 tokens x (4 * EPW) experts.  Lanes are tokens; wave w runs the
+// EPW chains of experts e0 + w*EPW + q side by side.  The x tile and the
+// router rows of each 64-wide hidden chunk are staged in LDS as fp32, double
+// buffered: the loads of chunk c+1 are in flight while chunk c is consumed,
+// and one barrier per chunk orders the buffers.  Each chain adds its products
+// in ascending hidden index, one fused multiply-add per element (the product
+// of two bf16 values is exact in fp32, so this equals a multiply then an add).
 template <int EPW>
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ w, int T, int H,
                                                        int E, float* __restrict__ logits) {
-    __shared__ float xs[kRouteTok][kRouteKC + 4];
+    constexpr int NE = kRouteWaves * EPW;                     // experts per block
+    constexpr int XPIECES = kRouteTok * (kRouteKC / 8);       // 16-byte pieces of the x tile
+    constexpr int WPIECES = NE * (kRouteKC / 8);              // 16-byte pieces of the w tile
+    constexpr int XITER = (XPIECES + 255) / 256;
+    constexpr int WITER = (WPIECES + 255) / 256;
+    __shared__ __attribute__((aligned(16))) float xs[2][kRouteTok][kRouteKC + 4];
+    __shared__ __attribute__((aligned(16))) float wsm[2][NE][kRouteKC];
+    const int tid = threadIdx.x;
     const int lane = lane_id();
-    const int wave = threadIdx.x >> 6;
+    const int wave = tid >> 6;
     const int t0 = blockIdx.x * kRouteTok;
-    const int e0 = __builtin_amdgcn_readfirstlane((int)((blockIdx.y * kRouteWaves + wave) * EPW));
-    float acc[EPW];
-#pragma unroll
-    for (int q = 0; q < EPW; ++q) acc[q] = 0.0f;
+    const int eb = blockIdx.y * NE;  // first expert of the block
 
-    for (int c = 0; c < H; c += kRouteKC) {
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < kRouteTok * (kRouteKC / 8); idx += blockDim.x) {
-            const int row = idx / (kRouteKC / 8);
-            const int piece = idx % (kRouteKC / 8);
-            const int tok = t0 + row;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (tok < T) v = *reinterpret_cast<const u32x4_t*>(x + (size_t)tok * H + c + piece * 8);
-            float* dst = &xs[row][piece * 8];
+    u32x4_t xq[XITER], wq[WITER];
+    auto load = [&](int c) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                dst[2 * j] = __uint_as_float(v[j] << 16);
-                dst[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
-            }
+        for (int it = 0; it < XITER; ++it) {
+            const int p = it * 256 + tid;
+            const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
+            // out-of-range rows load row 0 and are zeroed by a select (no load under a branch)
+            const bool ok = p < XPIECES && t0 + row < T;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (size_t)(ok ? t0 + row : 0) * H + c + (ok ? piece : 0) * 8);
+            xq[it] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
         }
-        __syncthreads();
-        for (int i = 0; i < kRouteKC; i += 8) {
-            const f32x4_t xa = *reinterpret_cast<const f32x4_t*>(&xs[lane][i]);
-            const f32x4_t xb = *reinterpret_cast<const f32x4_t*>(&xs[lane][i + 4]);
 #pragma unroll
-            for (int q = 0; q < EPW; ++q) {
-                if (e0 + q < E) {
-                    const u32x4_t wv =
-                        *reinterpret_cast<const u32x4_t*>(w + (size_t)(e0 + q) * H + c + i);
-                    float a = acc[q];
-                    a = __builtin_fmaf(xa[0], __uint_as_float(wv[0] << 16), a);
-                    a = __builtin_fmaf(xa[1], __uint_as_float(wv[0] & 0xFFFF0000u), a);
-                    a = __builtin_fmaf(xa[2], __uint_as_float(wv[1] << 16), a);
-                    a = __builtin_fmaf(xa[3], __uint_as_float(wv[1] & 0xFFFF0000u), a);
-                    a = __builtin_fmaf(xb[0], __uint_as_float(wv[2] << 16), a);
-                    a = __builtin_fmaf(xb[1], __uint_as_float(wv[2] & 0xFFFF0000u), a);
-                    a = __builtin_fmaf(xb[2], __uint_as_float(wv[3] << 16), a);
-                    a = __builtin_fmaf(xb[3], __uint_as_float(wv[3] & 0xFFFF0000u), a);
-                    acc[q] = a;
+        for (int it = 0; it < WITER; ++it) {
+            const int p = it * 256 + tid;
+            const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
+            const bool ok = p < WPIECES && eb + row < E;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(w + (size_t)(ok ? eb + row : 0) * H + c + (ok ? piece : 0) * 8);
+            wq[it] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < XITER; ++it) {
+            const int p = it * 256 + tid;
+            if (p < XPIECES) {
+                const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
+                float* dst = &xs[buf][row][piece * 8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    dst[2 * j] = __uint_as_float(xq[it][j] << 16);
+                    dst[2 * j + 1] = __uint_as_float(xq[it][j] & 0xFFFF0000u);
                 }
             }
         }
+#pragma unroll
+        for (int it = 0; it < WITER; ++it) {
+            const int p = it * 256 + tid;
+            if (p < WPIECES) {
+                const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
+                float* dst = &wsm[buf][row][piece * 8];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    dst[2 * j] = __uint_as_float(wq[it][j] << 16);
+                    dst[2 * j + 1] = __uint_as_float(wq[it][j] & 0xFFFF0000u);
+                }
+            }
+        }
+    };
+
+    float acc[EPW];
+#pragma unroll
+    for (int q = 0; q < EPW; ++q) acc[q] = 0.0f;
+    const int nch = H / kRouteKC;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nch) load((c + 1) * kRouteKC);
+#pragma unroll
+        for (int i = 0; i < kRouteKC; i += 4) {
+            const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[buf][lane][i]);
+#pragma unroll
+            for (int q = 0; q < EPW; ++q) {
+                const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(&wsm[buf][wave * EPW + q][i]);
+                float a = acc[q];
+                a = __builtin_fmaf(xv[0], wv[0], a);
+                a = __builtin_fmaf(xv[1], wv[1], a);
+                a = __builtin_fmaf(xv[2], wv[2], a);
+                a = __builtin_fmaf(xv[3], wv[3], a);
+                acc[q] = a;
+            }
+        }
+        if (c + 1 < nch) store(buf ^ 1);
+        __syncthreads();
     }
     const int t = t0 + lane;
     if (t < T) {
 #pragma unroll
-        for (int q = 0; q < EPW; ++q)
-            if (e0 + q < E) logits[(size_t)t * E + e0 + q] = acc[q];
+        for (int q = 0; q < EPW; ++q) {
+            const int e = eb + wave * EPW + q;
+            if (e < E) logits[(size_t)t * E + e] = acc[q];
+        }
     }
 }
 

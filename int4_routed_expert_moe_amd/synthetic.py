@@ -11,7 +11,10 @@ contains") and the Kimi-K3 latent block (3584-wide latent, RMSNorm before a
 3584->7168 up-projection; Kimi-K3 latent MoE page, Parameters table and Code).
 Value distributions:
   x            bf16( N(0,1) )
-  router W     bf16( N(0, 0.02) ),  correction bias f32 U(-0.1, 0.1)
+  router W     bf16( N(0, 0.02) ),  correction bias f32 U(-b, b) with b = 0.1 on the
+               tiny layer and b = 0.003 on the K2.5/K3-shaped layers, whose routing is
+               specified as uniform (with b = 0.1 the bias, not the logits, would decide
+               most selections: the top scores sit near 1 where the sigmoid is flat)
   expert W     uniform random bytes (two int4 per byte -> uniform on [-8, 7]),
                bf16 group-32 scales U(0.005, 0.02)
   shared/latent bf16( N(0, 1/sqrt(fan_in)) ), RMSNorm gain bf16 U(0.9, 1.1)
@@ -33,15 +36,15 @@ T_ZIPF_CAL, T_SAMPLE = 15, 16
 
 CONFIGS = {
     1: dict(id=1, name="tiny", T=64, H=256, E=16, k=2, I=128, shared_I=128, L=None,
-            mode="bf16", layer_seed=1, x_seed=1, rms_eps=1e-6),
+            mode="bf16", layer_seed=1, x_seed=1, rms_eps=1e-6, bias_range=0.1),
     2: dict(id=2, name="k25_decode", T=64, H=7168, E=384, k=8, I=2048, shared_I=2048, L=None,
-            mode="bf16", layer_seed=2, x_seed=2, rms_eps=1e-6),
+            mode="bf16", layer_seed=2, x_seed=2, rms_eps=1e-6, bias_range=0.003),
     3: dict(id=3, name="k25_prefill", T=8192, H=7168, E=384, k=8, I=2048, shared_I=2048, L=None,
-            mode="bf16", layer_seed=2, x_seed=3, rms_eps=1e-6),
+            mode="bf16", layer_seed=2, x_seed=3, rms_eps=1e-6, bias_range=0.003),
     4: dict(id=4, name="k25_exact_zipf", T=4096, H=7168, E=384, k=8, I=2048, shared_I=None,
-            L=None, mode="exact", layer_seed=2, x_seed=4, rms_eps=1e-6, zipf=True),
+            L=None, mode="exact", layer_seed=2, x_seed=4, rms_eps=1e-6, zipf=True, bias_range=0.003),
     5: dict(id=5, name="k3_latent", T=2048, H=7168, E=384, k=8, I=2048, shared_I=2048, L=3584,
-            mode="bf16", layer_seed=5, x_seed=5, rms_eps=1e-6),
+            mode="bf16", layer_seed=5, x_seed=5, rms_eps=1e-6, bias_range=0.003),
 }
 
 
@@ -118,8 +121,8 @@ def gen_x(cfg, T=None):
 def gen_router(cfg):
     s = cfg["layer_seed"]
     w = normal_bf16(rng(s, T_ROUTER_W), (cfg["E"], cfg["H"]), 0.02)
-    b = (rng(s, T_ROUTER_B).random(cfg["E"], dtype=np.float32) * np.float32(0.2)
-         - np.float32(0.1)).astype(np.float32)
+    br = np.float32(cfg.get("bias_range", 0.1))
+    b = (rng(s, T_ROUTER_B).random(cfg["E"], dtype=np.float32) * (np.float32(2) * br) - br).astype(np.float32)
     return w, b
 
 

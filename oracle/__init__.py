@@ -422,13 +422,16 @@ def layer_tokens(inp, tokens, topk_idx=None, topk_w=None, want_intermediates=Fal
             s = inp["shared"]
             sh_out = dense_swiglu_bf16(x, s["wg"], s["wu"], s["wd"])
             inter["shared"] = sh_out
+        routed = combine_bf16(r["y"].reshape(n, k, Hr), w, None)
+        inter["routed"] = routed
         if lat is None:
             out = combine_bf16(r["y"].reshape(n, k, Hr), w, sh_out)
         else:
-            routed = combine_bf16(r["y"].reshape(n, k, Hr), w, None)
             nrm = rmsnorm_bf16(routed, lat["gain"], cfg["rms_eps"])
             out = linear_bf16(nrm, lat["w_up"], add=sh_out)
-            inter.update({"x_lat": xr, "routed": routed, "normed": nrm})
+            inter.update({"x_lat": xr, "normed": nrm})
+            if want_intermediates:
+                inter["up"] = linear_bf16(nrm, lat["w_up"])
         inter.update(r)
     assert out.shape[1] == H
     return (out, inter) if want_intermediates else out

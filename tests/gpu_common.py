@@ -59,15 +59,21 @@ def bf16_to_f64(a):
     return ((np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
 
 
-def assert_bf16_close(got, ref, what="", atol_rms=1e-2, rtol=2e-2):
-    """bf16-path tolerance: |g - r| <= atol_rms * rms(r) + rtol * |r| elementwise
-    (the bound is scaled by the reference's rms so it means the same at any output scale)."""
+def assert_bf16_close(got, ref, what="", atol_rms=1e-2, rtol=2e-2, addends=()):
+    """bf16-path tolerance: |g - r| <= atol_rms * rms(r) + rtol * m elementwise, with
+    m = |r|, or, for an output that is the bf16 sum of bf16 terms (the shared-expert
+    add), m = the sum of the terms' magnitudes: one bf16 step of a term survives a
+    cancellation in the sum.  The absolute part is scaled by the reference's rms so
+    it means the same at any output scale."""
     g = bf16_to_f64(got)
     r = bf16_to_f64(ref)
     assert g.shape == r.shape, (g.shape, r.shape)
     rms = float(np.sqrt(np.mean(r * r))) or 1.0
     err = np.abs(g - r)
-    bound = atol_rms * rms + rtol * np.abs(r)
+    mag = np.abs(r)
+    if addends:
+        mag = np.maximum(mag, sum(np.abs(bf16_to_f64(a)) for a in addends))
+    bound = atol_rms * rms + rtol * mag
     bad = err > bound
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)

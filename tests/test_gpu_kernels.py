@@ -67,8 +67,8 @@ def test_sigmoid_matches_oracle_on_a_sweep(m):
     """Route with one expert row per logit value: the selected weight (renormalise
     off, k=E) is the sigmoid of that logit, bit for bit."""
     say("sigmoid sweep")
-    H, E = 128, 64
-    vals = np.linspace(-90, 90, 64 * 97, dtype=np.float32)
+    H, E = 128, 16
+    vals = np.linspace(-90, 90, 16 * 389, dtype=np.float32)
     # logit = x[0] * w[e,0] with x = (1, 0, ...): w[e,0] carries the value (bf16-rounded)
     wv = refmath.bf16_from_f32(vals)
     T = 1
@@ -175,7 +175,7 @@ def _routing(g, T, E, k, skew=False):
     (64, 256, 128, 16, 2, False, 0),     # tiny workload shape
     (37, 512, 256, 8, 3, False, 1),      # ragged tail, one tile per expert
     (300, 256, 128, 4, 2, True, 2),      # many rows per expert (several tiles) and empty experts
-    (700, 384, 256, 6, 2, False, 3),     # largest tile height
+    (700, 512, 256, 6, 2, False, 3),     # largest tile height
 ])
 def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     say(f"grouped bf16 T={T} H={H} I={I} E={E} k={k}")

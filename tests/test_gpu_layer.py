@@ -76,7 +76,12 @@ def test_layer_parity(cfg_id):
             assert_bf16_close(np_bf16(ws["routed"])[toks], inter["routed"], "routed")
         if inp.get("shared") is not None:
             assert_bf16_close(np_bf16(ws["shared_out"])[toks], inter["shared"], "shared")
-        worst = assert_bf16_close(np_bf16(out)[toks], ref, "out")
+        terms = ()
+        if inp.get("shared") is not None:
+            terms = (inter["up"] if cfg.get("L") else inter["routed"], inter["shared"])
+        else:
+            assert_bf16_close(np_bf16(out)[toks], inter["routed"], "routed out")
+        worst = assert_bf16_close(np_bf16(out)[toks], ref, "out", addends=terms)
         say(f"workload {cfg_id}: worst |err|/rms = {worst:.3g}")
 
 
@@ -102,8 +107,8 @@ def test_layer_edge_token_counts():
         x = inp["x"][:T]
         out = L.forward(bf16_dev(x))
         torch.cuda.synchronize()
-        ref = oracle.layer_tokens(dict(inp, x=x), np.arange(T))
-        assert_bf16_close(np_bf16(out), ref, f"T={T}")
+        ref, inter = oracle.layer_tokens(dict(inp, x=x), np.arange(T), want_intermediates=True)
+        assert_bf16_close(np_bf16(out), ref, f"T={T}", addends=(inter["routed"], inter["shared"]))
     # empty input is a no-op
     out = L.forward(bf16_dev(inp["x"][:0]))
     assert out.shape[0] == 0
