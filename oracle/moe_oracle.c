@@ -155,10 +155,14 @@ void oracle_unpack_int4(const uint8_t* packed, int N, int K, int8_t* q_out) {
 /* retaining original affinities" (bias added for ranking only),             */
 /* "MoEGate.forward: ( , topk idx)" and "Normalize the selected routing      */
 /* affinities" (divide by the sum of the selected affinities plus 1e-20).    */
-/* Readings: logits in fp32, summed in ascending hidden index from 0; ties   */
-/* in the biased score go to the lower expert index; slots are in rank       */
-/* order; routed scaling factor 1; one expert group.                         */
+/* Readings: logits in fp32 in a fixed two-level order: each block of 64    */
+/* consecutive hidden elements is summed from 0 in ascending index, and the  */
+/* block sums are added from 0 in ascending block order (H is a multiple of  */
+/* 64); ties in the biased score go to the lower expert index; slots are in  */
+/* rank order; routed scaling factor 1; one expert group.                    */
 /* ------------------------------------------------------------------------- */
+
+#define ORC_LOGIT_BLOCK 64
 
 void oracle_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, int E,
                           float* logits /* [T,E] */) {
@@ -167,9 +171,14 @@ void oracle_router_logits(const uint16_t* x, const uint16_t* wr, int T, int H, i
         const uint16_t* xr = x + (size_t)t * H;
         for (int e = 0; e < E; ++e) {
             const uint16_t* wrow = wr + (size_t)e * H;
-            float acc = 0.0f;
-            for (int i = 0; i < H; ++i) acc = acc + bf16_to_f32(xr[i]) * bf16_to_f32(wrow[i]);
-            logits[(size_t)t * E + e] = acc;
+            float total = 0.0f;
+            for (int b = 0; b < H; b += ORC_LOGIT_BLOCK) {
+                float part = 0.0f;
+                for (int i = b; i < b + ORC_LOGIT_BLOCK; ++i)
+                    part = part + bf16_to_f32(xr[i]) * bf16_to_f32(wrow[i]);
+                total = total + part;
+            }
+            logits[(size_t)t * E + e] = total;
         }
     }
 }

@@ -32,7 +32,9 @@ def test_one_hot_logits_are_router_weights():
     np.testing.assert_array_equal(l, refmath.bf16_to_f32(w[:, cols]).T)
 
 
-def test_logits_within_sequential_fp32_bound():
+def test_logits_within_two_level_fp32_bound():
+    """Blocks of 64 summed in order, then the H/64 block sums in order: the
+    rounding error is at most gamma_(64 + H/64) times the sum of |products|."""
     T, H, E = 6, 7168, 24
     x, w, _ = _rand_router(T, H, E, 1)
     l = oracle.router_logits(x, w).astype(np.float64)
@@ -40,9 +42,30 @@ def test_logits_within_sequential_fp32_bound():
     wf = refmath.bf16_to_f32(w).astype(np.float64)
     exact = xf @ wf.T
     u = 2.0 ** -24
-    gamma = H * u / (1 - H * u)
+    n = 64 + H // 64
+    gamma = n * u / (1 - n * u)
     bound = gamma * (np.abs(xf) @ np.abs(wf).T)
     assert np.all(np.abs(l - exact) <= bound)
+
+
+def test_logits_follow_the_two_level_order():
+    """A block whose sum cancels to zero exactly, then a small term: with a single
+    running sum the small term would be absorbed by the large partial sums; with
+    block sums it survives exactly."""
+    H, E = 128, 1
+    x = np.zeros((1, H), np.uint16)
+    w = np.zeros((E, H), np.uint16)
+    big, small = 2.0 ** 30, 1.0
+    vals = np.zeros(H, np.float32)
+    vals[0], vals[1], vals[64] = big, -big, small
+    x[0] = refmath.bf16_from_f32(vals)
+    w[0] = refmath.bf16_from_f32(np.ones(H, np.float32))
+    assert oracle.router_logits(x, w)[0, 0] == 1.0
+    # order inside a block is ascending: (big + small) - big loses the small term
+    vals2 = np.zeros(H, np.float32)
+    vals2[0], vals2[1], vals2[2] = big, small, -big
+    x[0] = refmath.bf16_from_f32(vals2)
+    assert oracle.router_logits(x, w)[0, 0] == 0.0
 
 
 def test_selection_is_stable_sort_of_biased_scores():
