@@ -72,16 +72,18 @@ const char* moe_last_error_detail(void);
  * "Independent sigmoid scores for the router", "Bias the choice of experts
  * while retaining original affinities", "MoEGate.forward: ( , topk idx)" and
  * "Normalize the selected routing affinities".
- *   l[t,e] = sum_i x[t,i] * w_router[e,i]   fp32, ascending i from 0
+ *   l[t,e] = sum over 64-wide hidden blocks b (ascending, from 0) of
+ *            the block sums (fp32, ascending index within the block, from 0)
  *   s = 1 / (1 + exp(-l))                   fp32, exp by the pinned
  *                                           Cody-Waite/Taylor-7 algorithm
  *   selection: the k largest s[t,e] + bias[e], ties to the lower e, in rank order
  *   topk_w[t,j] = s_sel / (sum_j s_sel + 1e-20)  (renormalize != 0; else s_sel)
  * x [T,H] bf16; w_router [E,H] bf16; bias [E] fp32;
  * out: topk_idx [T,k] int32, topk_w [T,k] fp32.
- * ws: device workspace of at least moe_route_workspace_bytes(T, E) bytes.
+ * ws: device workspace of at least moe_route_workspace_bytes(T, H, E) bytes,
+ * 16-byte aligned (it holds the logits and an fp32 copy of w_router).
  * Results are bit-exact and deterministic. */
-size_t moe_route_workspace_bytes(int T, int E);
+size_t moe_route_workspace_bytes(int T, int H, int E);
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,
               int k, int renormalize, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
               void* stream);

@@ -6,10 +6,9 @@
 // affinities").
 //
 // The selected indices must be reproducible bit for bit, so every logit is
-// one fp32 chain summed in ascending hidden index from 0 (no split, no
-// matrix cores: their internal summation order is unspecified).  Lanes are
-// tokens and each wave runs EPW such chains (one per expert) side by side;
-// the expert rows are wave-uniform LDS reads (broadcasts).
+// summed in one fixed fp32 order: each 64-element hidden block from 0 in
+// ascending index, then the block sums from 0 in ascending block order (no
+// matrix cores: their internal summation order is unspecified).
 #include "moe_common.h"
 
 namespace {
@@ -18,82 +17,83 @@ constexpr int kRouteTok = 64;   // tokens per block (one per lane)
 constexpr int kRouteKC = 64;    // hidden elements staged per LDS chunk
 constexpr int kRouteWaves = 4;
 
+// Router rows bf16 -> fp32 (exact), so the logits kernel can read them as
+// wave-uniform scalar loads with no per-element conversion.
+__global__ __launch_bounds__(256) void k_router_w_f32(const uint16_t* __restrict__ w, long n,
+                                                      float* __restrict__ wf) {
+    const long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (i >= n) return;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(w + i);
+    f32x4_t lo, hi;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        lo[2 * j] = __uint_as_float(v[j] << 16);
+        lo[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
+        hi[2 * j] = __uint_as_float(v[2 + j] << 16);
+        hi[2 * j + 1] = __uint_as_float(v[2 + j] & 0xFFFF0000u);
+    }
+    *reinterpret_cast<f32x4_t*>(wf + i) = lo;
+    *reinterpret_cast<f32x4_t*>(wf + i + 4) = hi;
+}
+
 // Logits of 64 tokens x (4 * EPW) experts.  Lanes are tokens; wave w runs the
-// EPW chains of experts e0 + w*EPW + q side by side.  The x tile and the
-// router rows of each 64-wide hidden chunk are staged in LDS as fp32, double
-// buffered: the loads of chunk c+1 are in flight while chunk c is consumed,
-// and one barrier per chunk orders the buffers.  Each chain adds its products
-// in ascending hidden index, one fused multiply-add per element (the product
-// of two bf16 values is exact in fp32, so this equals a multiply then an add).
+// EPW chains of experts eb + w*EPW + q side by side.  The x tile of each
+// 64-wide hidden chunk is staged in LDS as fp32, double buffered (the loads of
+// chunk c+1 are in flight while chunk c is consumed; one barrier per chunk);
+// the fp32 router rows are wave-uniform and come through the scalar cache.
+// Each chain adds its products in ascending hidden index, one fused
+// multiply-add per element (the product of two bf16 values is exact in fp32,
+// so this equals a multiply then an add).
 template <int EPW>
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x,
-                                                       const uint16_t* __restrict__ w, int T, int H,
+                                                       const float* __restrict__ wf, int T, int H,
                                                        int E, float* __restrict__ logits) {
-    constexpr int NE = kRouteWaves * EPW;                     // experts per block
-    constexpr int XPIECES = kRouteTok * (kRouteKC / 8);       // 16-byte pieces of the x tile
-    constexpr int WPIECES = NE * (kRouteKC / 8);              // 16-byte pieces of the w tile
-    constexpr int XITER = (XPIECES + 255) / 256;
-    constexpr int WITER = (WPIECES + 255) / 256;
+    constexpr int XPIECES = kRouteTok * (kRouteKC / 8);  // 16-byte pieces of the x tile
+    constexpr int XITER = XPIECES / 256;
     __shared__ __attribute__((aligned(16))) float xs[2][kRouteTok][kRouteKC + 4];
-    __shared__ __attribute__((aligned(16))) float wsm[2][NE][kRouteKC];
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid >> 6;
     const int t0 = blockIdx.x * kRouteTok;
-    const int eb = blockIdx.y * NE;  // first expert of the block
+    const int e0 = __builtin_amdgcn_readfirstlane((int)((blockIdx.y * kRouteWaves + wave) * EPW));
 
-    u32x4_t xq[XITER], wq[WITER];
+    const float* wq[EPW];
+#pragma unroll
+    for (int q = 0; q < EPW; ++q) wq[q] = wf + (size_t)min(e0 + q, E - 1) * H;  // rows past E: never stored
+
+    u32x4_t xq[XITER];
     auto load = [&](int c) {
 #pragma unroll
         for (int it = 0; it < XITER; ++it) {
             const int p = it * 256 + tid;
             const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
-            // out-of-range rows load row 0 and are zeroed by a select (no load under a branch)
-            const bool ok = p < XPIECES && t0 + row < T;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (size_t)(ok ? t0 + row : 0) * H + c + (ok ? piece : 0) * 8);
+            // rows past T load row 0 and are zeroed by a select (no load under a branch)
+            const bool ok = t0 + row < T;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (size_t)(ok ? t0 + row : 0) * H + c + piece * 8);
             xq[it] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int it = 0; it < WITER; ++it) {
-            const int p = it * 256 + tid;
-            const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
-            const bool ok = p < WPIECES && eb + row < E;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(w + (size_t)(ok ? eb + row : 0) * H + c + (ok ? piece : 0) * 8);
-            wq[it] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
         }
     };
     auto store = [&](int buf) {
 #pragma unroll
         for (int it = 0; it < XITER; ++it) {
             const int p = it * 256 + tid;
-            if (p < XPIECES) {
-                const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
-                float* dst = &xs[buf][row][piece * 8];
+            const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
+            f32x4_t lo, hi;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    dst[2 * j] = __uint_as_float(xq[it][j] << 16);
-                    dst[2 * j + 1] = __uint_as_float(xq[it][j] & 0xFFFF0000u);
-                }
+            for (int j = 0; j < 2; ++j) {
+                lo[2 * j] = __uint_as_float(xq[it][j] << 16);
+                lo[2 * j + 1] = __uint_as_float(xq[it][j] & 0xFFFF0000u);
+                hi[2 * j] = __uint_as_float(xq[it][2 + j] << 16);
+                hi[2 * j + 1] = __uint_as_float(xq[it][2 + j] & 0xFFFF0000u);
             }
-        }
-#pragma unroll
-        for (int it = 0; it < WITER; ++it) {
-            const int p = it * 256 + tid;
-            if (p < WPIECES) {
-                const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
-                float* dst = &wsm[buf][row][piece * 8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    dst[2 * j] = __uint_as_float(wq[it][j] << 16);
-                    dst[2 * j + 1] = __uint_as_float(wq[it][j] & 0xFFFF0000u);
-                }
-            }
+            *reinterpret_cast<f32x4_t*>(&xs[buf][row][piece * 8]) = lo;
+            *reinterpret_cast<f32x4_t*>(&xs[buf][row][piece * 8 + 4]) = hi;
         }
     };
 
-    float acc[EPW];
+    float acc[EPW], total[EPW];
 #pragma unroll
-    for (int q = 0; q < EPW; ++q) acc[q] = 0.0f;
+    for (int q = 0; q < EPW; ++q) total[q] = 0.0f;
     const int nch = H / kRouteKC;
     load(0);
     store(0);
@@ -101,12 +101,15 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     for (int c = 0; c < nch; ++c) {
         const int buf = c & 1;
         if (c + 1 < nch) load((c + 1) * kRouteKC);
+        const int cbase = c * kRouteKC;
 #pragma unroll
+        for (int q = 0; q < EPW; ++q) acc[q] = 0.0f;
+#pragma unroll 2
         for (int i = 0; i < kRouteKC; i += 4) {
             const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[buf][lane][i]);
 #pragma unroll
             for (int q = 0; q < EPW; ++q) {
-                const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(&wsm[buf][wave * EPW + q][i]);
+                const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(wq[q] + cbase + i);
                 float a = acc[q];
                 a = __builtin_fmaf(xv[0], wv[0], a);
                 a = __builtin_fmaf(xv[1], wv[1], a);
@@ -115,6 +118,8 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
                 acc[q] = a;
             }
         }
+#pragma unroll
+        for (int q = 0; q < EPW; ++q) total[q] = total[q] + acc[q];  // block sums in ascending order
         if (c + 1 < nch) store(buf ^ 1);
         __syncthreads();
     }
@@ -122,16 +127,80 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     if (t < T) {
 #pragma unroll
         for (int q = 0; q < EPW; ++q) {
-            const int e = eb + wave * EPW + q;
-            if (e < E) logits[(size_t)t * E + e] = acc[q];
+            const int e = e0 + q;
+            if (e < E) logits[(size_t)t * E + e] = total[q];
+        }
+    }
+}
+
+// Block sums of the logits for few tokens: P[t][b][e] = sum over the 64-wide
+// hidden block b in ascending index.  Every (token, expert, block) is an
+// independent 64-long chain, so all of them run in parallel; the top-k kernel
+// adds the block sums of each logit in ascending block order.
+// Grid: (H/64, ceil(E/64), ceil(T/64)); each thread owns 4 tokens x 4 experts.
+__global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ w, int T, int H,
+                                                         int E, float* __restrict__ P) {
+    __shared__ __attribute__((aligned(16))) float xs[kRouteKC][64 + 4];  // [i][t]
+    __shared__ __attribute__((aligned(16))) float ws[kRouteKC][64 + 4];  // [i][e]
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const int e0 = blockIdx.y * 64;
+    const int t0 = blockIdx.z * 64;
+    const int NB = H / kRouteKC;
+    // stage: 64 rows x 64 elements of x and of w, transposed to [i][row]
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int p = it * 256 + tid;          // 512 pieces of 8 elements per matrix
+        const int row = p >> 3, piece = p & 7;
+        const bool okx = t0 + row < T, okw = e0 + row < E;
+        const u32x4_t vx = *reinterpret_cast<const u32x4_t*>(x + (size_t)(okx ? t0 + row : 0) * H + b * kRouteKC + piece * 8);
+        const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(w + (size_t)(okw ? e0 + row : 0) * H + b * kRouteKC + piece * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            xs[piece * 8 + 2 * j][row] = okx ? __uint_as_float(vx[j] << 16) : 0.0f;
+            xs[piece * 8 + 2 * j + 1][row] = okx ? __uint_as_float(vx[j] & 0xFFFF0000u) : 0.0f;
+            ws[piece * 8 + 2 * j][row] = okw ? __uint_as_float(vw[j] << 16) : 0.0f;
+            ws[piece * 8 + 2 * j + 1][row] = okw ? __uint_as_float(vw[j] & 0xFFFF0000u) : 0.0f;
+        }
+    }
+    __syncthreads();
+    const int tt = tid >> 4, te = tid & 15;
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < kRouteKC; ++i) {
+        const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[i][4 * tt]);
+        const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(&ws[i][4 * te]);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[a][c] = __builtin_fmaf(xv[a], wv[c], acc[a][c]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int t = t0 + 4 * tt + a;
+        if (t >= T) continue;
+        float* dst = P + ((size_t)t * NB + b) * E + e0 + 4 * te;
+        if (e0 + 4 * te + 3 < E) {
+            *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (e0 + 4 * te + c < E) dst[c] = acc[a][c];
         }
     }
 }
 
 // One wave per token: scores, biased ranking keys, k rounds of a wave-wide
 // arg-max (larger key, then lower expert index), renormalisation in rank order.
+// With nb > 0 the logits are summed here from block sums P[t][b][e] in
+// ascending block order; otherwise they are read from logits[t][e].
 template <int NQ>
-__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int nb,
                                                     const float* __restrict__ bias, int T, int E,
                                                     int k, int renormalize,
                                                     int32_t* __restrict__ topk_idx,
@@ -141,11 +210,37 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     if (t >= T) return;
     float s[NQ], key[NQ];
     uint32_t taken = 0;
+    float lg[NQ];
+    if (nb > 0) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) lg[q] = 0.0f;
+        const float* Pt = logits + (size_t)t * nb * E;
+        constexpr int BB = 8;  // block sums loaded per batch (all loads issued before the adds)
+        int b = 0;
+        for (; b + BB <= nb; b += BB) {
+            float v[BB][NQ];
+#pragma unroll
+            for (int u = 0; u < BB; ++u)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) v[u][q] = Pt[(size_t)(b + u) * E + min(lane + MOE_WAVE * q, E - 1)];
+#pragma unroll
+            for (int u = 0; u < BB; ++u)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) lg[q] = lg[q] + v[u][q];
+        }
+        for (; b < nb; ++b) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) lg[q] = lg[q] + Pt[(size_t)b * E + min(lane + MOE_WAVE * q, E - 1)];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) lg[q] = logits[(size_t)t * E + min(lane + MOE_WAVE * q, E - 1)];
+    }
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int e = lane + MOE_WAVE * q;
         if (e < E) {
-            s[q] = moe_sigmoid(logits[(size_t)t * E + e]);
+            s[q] = moe_sigmoid(lg[q]);
             key[q] = s[q] + bias[e];
         } else {
             s[q] = 0.0f;
@@ -193,17 +288,26 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
 }
 
 template <int NQ>
-void launch_topk(const float* logits, const float* bias, int T, int E, int k, int renorm,
+void launch_topk(const float* logits, int nb, const float* bias, int T, int E, int k, int renorm,
                  int32_t* idx, float* w, hipStream_t st) {
-    hipLaunchKernelGGL(k_route_topk<NQ>, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, T, E, k,
-                       renorm, idx, w);
+    hipLaunchKernelGGL(k_route_topk<NQ>, dim3((T + 3) / 4), dim3(256), 0, st, logits, nb, bias, T, E,
+                       k, renorm, idx, w);
 }
+
+// Few tokens: all (token, expert, block) sums in parallel, summed in the top-k
+// kernel.  Many tokens: one fused pass keeps each logit's running total.
+constexpr int kPartialsMaxT = 256;
 
 }  // namespace
 
-extern "C" size_t moe_route_workspace_bytes(int T, int E) {
-    if (T <= 0 || E <= 0) return 0;
-    return (size_t)T * (size_t)E * sizeof(float);
+// Few tokens: block sums [T, H/64, E] fp32.  Many tokens: logits [T, E] fp32,
+// then the fp32 router rows [E, H] (256-byte aligned).
+static size_t logits_bytes(int T, int E) { return (((size_t)T * (size_t)E * sizeof(float)) + 255) & ~(size_t)255; }
+
+extern "C" size_t moe_route_workspace_bytes(int T, int H, int E) {
+    if (T <= 0 || E <= 0 || H <= 0) return 0;
+    if (T <= kPartialsMaxT) return (size_t)T * (size_t)(H / kRouteKC) * (size_t)E * sizeof(float);
+    return logits_bytes(T, E) + (size_t)E * (size_t)H * sizeof(float);
 }
 
 extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
@@ -221,26 +325,32 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const floa
         return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
     if (!aligned16(x) || !aligned16(w_router))
         return fail(MOE_ERR_INVALID_ARG, "moe_route: x and w_router must be 16-byte aligned");
-    if (!ws || ws_bytes < moe_route_workspace_bytes(T, E))
+    if (!ws || ws_bytes < moe_route_workspace_bytes(T, H, E))
         return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu bytes", ws_bytes,
-                    moe_route_workspace_bytes(T, E));
+                    moe_route_workspace_bytes(T, H, E));
+    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "moe_route: workspace must be 16-byte aligned");
     hipStream_t st = as_stream(stream);
     float* logits = static_cast<float*>(ws);
     const int tb = (T + kRouteTok - 1) / kRouteTok;
-    if (T <= 256) {
-        dim3 grid(tb, (E + kRouteWaves - 1) / kRouteWaves);
-        hipLaunchKernelGGL(k_router_logits<1>, grid, dim3(256), 0, st, x, w_router, T, H, E, logits);
+    int nb = 0;
+    if (T <= kPartialsMaxT) {
+        nb = H / kRouteKC;
+        dim3 grid(nb, (E + 63) / 64, tb);
+        hipLaunchKernelGGL(k_router_partials, grid, dim3(256), 0, st, x, w_router, T, H, E, logits);
     } else {
+        float* wf = reinterpret_cast<float*>(static_cast<char*>(ws) + logits_bytes(T, E));
+        const long nw = (long)E * H;
+        hipLaunchKernelGGL(k_router_w_f32, dim3((unsigned)((nw / 8 + 255) / 256)), dim3(256), 0, st, w_router, nw, wf);
         dim3 grid(tb, (E + kRouteWaves * 8 - 1) / (kRouteWaves * 8));
-        hipLaunchKernelGGL(k_router_logits<8>, grid, dim3(256), 0, st, x, w_router, T, H, E, logits);
+        hipLaunchKernelGGL(k_router_logits<8>, grid, dim3(256), 0, st, x, wf, T, H, E, logits);
     }
     int rc = launch_status("moe_route logits");
     if (rc) return rc;
     const int nq = (E + MOE_WAVE - 1) / MOE_WAVE;
-    if (nq <= 1) launch_topk<1>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 2) launch_topk<2>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 4) launch_topk<4>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 8) launch_topk<8>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else launch_topk<16>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    if (nq <= 1) launch_topk<1>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    else if (nq <= 2) launch_topk<2>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    else if (nq <= 4) launch_topk<4>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    else if (nq <= 8) launch_topk<8>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    else launch_topk<16>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
     return launch_status("moe_route topk");
 }

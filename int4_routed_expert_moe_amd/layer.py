@@ -74,7 +74,7 @@ class MoELayer:
         S = T * k
         exact = self.mode == _m.MOE_MODE_EXACT_I8
         w = {
-            "route_ws": torch.empty(max(1, _m.moe_route_workspace_bytes(T, E)), dtype=torch.uint8, device=dev),
+            "route_ws": torch.empty(max(1, _m.moe_route_workspace_bytes(T, self.H, E)), dtype=torch.uint8, device=dev),
             "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
             "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
             "counts": torch.empty(E, dtype=torch.int32, device=dev),

@@ -38,7 +38,7 @@ EXPORTS = {
     "moe_abi_version": ([], _I),
     "moe_status_string": ([_I], ctypes.c_char_p),
     "moe_last_error_detail": ([], ctypes.c_char_p),
-    "moe_route_workspace_bytes": ([_I, _I], _SZ),
+    "moe_route_workspace_bytes": ([_I, _I, _I], _SZ),
     "moe_route": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "moe_permute": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "moe_quant_act_int8": ([_P, _I, _I, _P, _P, _P], _I),
@@ -96,8 +96,8 @@ def moe_abi_version() -> int:
     return _lib.moe_abi_version()
 
 
-def moe_route_workspace_bytes(T, E) -> int:
-    return _lib.moe_route_workspace_bytes(T, E)
+def moe_route_workspace_bytes(T, H, E) -> int:
+    return _lib.moe_route_workspace_bytes(T, H, E)
 
 
 def moe_route(x, w_router, bias, k, renormalize, topk_idx, topk_w, ws):

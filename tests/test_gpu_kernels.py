@@ -50,7 +50,7 @@ def test_route_bitexact(m, T, H, E, k, seed):
     ridx, rw = oracle.route(x, w, b, k, True)
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(m.moe_route_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(m.moe_route_workspace_bytes(T, H, E), dtype=torch.uint8, device="cuda")
     m.moe_route(bf16_dev(x), bf16_dev(w), torch.from_numpy(b).cuda(), k, True, idx, wt, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
@@ -81,7 +81,7 @@ def test_sigmoid_matches_oracle_on_a_sweep(m):
         ridx, rw = oracle.route(x, w, b, E, False)
         idx = torch.empty((T, E), dtype=torch.int32, device="cuda")
         wt = torch.empty((T, E), dtype=torch.float32, device="cuda")
-        ws = torch.empty(m.moe_route_workspace_bytes(T, E), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(m.moe_route_workspace_bytes(T, H, E), dtype=torch.uint8, device="cuda")
         m.moe_route(bf16_dev(x), bf16_dev(w), torch.from_numpy(b).cuda(), E, False, idx, wt, ws)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
