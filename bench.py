@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device-to-device copy of this many MiB (3 times), the reference "
                          "kernel for scaling HBM byte counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of a run with "
+                         "--calibrate-copy into profiles/<call>_<workload>_traffic.json")
     return ap.parse_args()
 
 
@@ -91,6 +94,61 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
+TRAFFIC_SOURCES = ["int4_routed_expert_moe_amd/csrc/grouped_gemm.hip", "int4_routed_expert_moe_amd/csrc/moe_common.h"]
+
+
+def _counter_means(folder, counter):
+    """Mean value per dispatch of one counter, per kernel, from rocprofv3 csv output."""
+    import csv
+    import glob
+    import re
+    vals = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            m = re.search(r"k_grouped(?:_skinny)?<(\d+), (\d+)", name)
+            if m:
+                key = "moe_int4_grouped_swiglu" if m.group(2) == "0" else "moe_int4_grouped_down"
+            elif "opy" in name:
+                key = ("copy", int(r["Grid_Size"]))
+            else:
+                continue
+            d = vals.setdefault(key, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    out = {k: float(np.mean(list(v.values()))) for k, v in vals.items() if not isinstance(k, tuple)}
+    copies = [k for k in vals if isinstance(k, tuple)]
+    if copies:  # the calibration copy is the copy launch with the largest grid (small staging copies also run)
+        out["copy"] = float(np.mean(list(vals[max(copies, key=lambda k: k[1])].values())))
+    return out
+
+
+def write_traffic(args, cfg):
+    """HBM bytes per launch of the grouped kernels from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled so that the plain copy of --calibrate-copy MiB reads and
+    writes exactly its size."""
+    fetch = _counter_means(args.traffic_from[0], "FETCH_SIZE")
+    write = _counter_means(args.traffic_from[1], "WRITE_SIZE")
+    copy_kib = args.calibrate_copy * 1024.0
+    ff, fw = copy_kib / fetch["copy"], copy_kib / write["copy"]
+    for call in ("moe_int4_grouped_swiglu", "moe_int4_grouped_down"):
+        if call not in fetch or call not in write:
+            continue
+        rec = {
+            "call": call, "workload": cfg["name"],
+            "fetch_bytes": fetch[call] * ff * 1024, "write_bytes": write[call] * fw * 1024,
+            "raw_fetch_kib": fetch[call], "raw_write_kib": write[call],
+            "copy_calibration": {"mib": args.calibrate_copy, "fetch_factor": ff, "write_factor": fw},
+            "sources": TRAFFIC_SOURCES, "source_sha": source_digest(TRAFFIC_SOURCES),
+        }
+        rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+        path = os.path.join(ROOT, "profiles", f"{call}_{cfg['name']}_traffic.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(f"{path}: {rec['bytes_per_launch'] / 1e9:.3f} GB per launch (copy factors {ff:.3f}, {fw:.3f})")
+
+
 def traffic_record(kernel, workload_name):
     """HBM traffic measured with rocprofv3 counters for this kernel and workload, if
     the record was taken on the current kernel source (else None)."""
@@ -109,11 +167,16 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-    import torch
     from int4_routed_expert_moe_amd import synthetic
+    cfg0 = synthetic.CONFIGS[args.workload]
+    if args.traffic_from:
+        if not args.calibrate_copy:
+            sys.exit("--traffic-from needs --calibrate-copy MIB, the copy size of the counted run")
+        write_traffic(args, cfg0)
+        return
+    import torch
     from int4_routed_expert_moe_amd.layer import MoELayer
 
-    cfg0 = synthetic.CONFIGS[args.workload]
     bias = None
     if cfg0.get("zipf"):
         bias = synthetic.load_bias_file(os.path.join(ROOT, "tests", "golden", "zipf_bias_k25.txt"))
