@@ -31,6 +31,8 @@
  *    `scale` is bf16 [N][K/32]; the weight is q * scale[n][i/32] (symmetric,
  *    no zero point).  A routed expert set stacks E such matrices:
  *    gate/up [E][I][H/2] + [E][I][H/32], down [E][H][I/2] + [E][H][I/32].
+ *    This is the checkpoint layout.  The grouped expert GEMMs read the same
+ *    bytes in the fragment layout made once by moe_int4_prepack (below).
  *  - Numerics of the routed GEMMs: operands are fp16 on the matrix cores.
  *    Activations must lie within the fp16 finite range (|v| < 65504; larger
  *    values saturate) and bf16 scales within [2^-14, 2^9] (outside it the
@@ -111,6 +113,24 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, i
 int moe_quant_act_int8(const uint16_t* x, int M, int K, int8_t* q, float* s, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Weight fragment layout for the grouped GEMMs (a layout step of this library,
+ * not of the method: the checkpoint buffers of "Kimi exact-generator
+ * adaptation", "The proposed substitution", load without any arithmetic
+ * conversion; this reorders their bytes once, exactly).
+ * Input: a stacked expert matrix in the checkpoint layout, packed [E][N][K/2],
+ * scale [E][N][K/32] bf16.  Output (same sizes, out of place): with
+ * nch = K/128, row group R = e*(N/16) + n/16 and chunk c,
+ *   packed_out[((R*nch + c)*64 + l)*16 + 4g + b] = packed[row 16(R%(N/16))+r of
+ *       expert e][64c + 16g + 4j + b],  lane l = r + 16j (r < 16, j < 4),
+ *       g < 4, b < 4   (1 KB per (R, c): 16 rows x 128 K, lane-major)
+ *   scale_out[((R*nch + c)*16 + r)*4 + g] = scale[row ...][4c + g]
+ * Nibble order inside each byte is unchanged.  N a multiple of 16, K of 128;
+ * packed buffers 16-byte and scale buffers 8-byte aligned; input and output
+ * must not overlap.  E == 0 is a no-op. */
+int moe_int4_prepack(const uint8_t* packed, const uint16_t* scale, int E, int N, int K,
+                     uint8_t* packed_out, uint16_t* scale_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Grouped gate/up projections + SwiGLU over the ragged expert segments
  * ("Kimi exact-generator adaptation", "The preserved forward form";
  * "Kimi K2.5 donor reference", record "SwiGLU-style gated feed-forward
@@ -124,6 +144,7 @@ int moe_quant_act_int8(const uint16_t* x, int M, int K, int8_t* q, float* s, voi
  *     G the exact int32 group dot product; h = silu(g) * u (fp32), quantised
  *     per row and group of 32 like moe_quant_act_int8 -> h = q_h [T*k, I]
  *     int8, h_scale = s_h [T*k, I/32] fp32.  Bit-exact.
+ * gate/up weights in the fragment layout of moe_int4_prepack.
  * Empty experts are skipped; rows of absent experts are not written. */
 int moe_int4_grouped_swiglu(int mode, const void* act, const float* act_scale,
                             const uint8_t* gate_packed, const uint16_t* gate_scale,
@@ -135,7 +156,8 @@ int moe_int4_grouped_swiglu(int mode, const void* act, const float* act_scale,
  * Grouped down projection: y[p] = h[p] . Wd[e]^T for every sorted row p.
  *   MOE_MODE_BF16: h [T*k, I] bf16 -> y [T*k, H] bf16 (= bf16 of the fp32 sum).
  *   MOE_MODE_EXACT_I8: h = q_h int8 with h_scale = s_h -> y [T*k, H] fp32,
- *     the fixed-order group combine as above.  Bit-exact. */
+ *     the fixed-order group combine as above.  Bit-exact.
+ * down weights in the fragment layout of moe_int4_prepack. */
 int moe_int4_grouped_down(int mode, const void* h, const float* h_scale, const uint8_t* down_packed,
                           const uint16_t* down_scale, const int32_t* offsets, int T, int k, int E,
                           int I, int H, void* y, void* stream);

@@ -18,29 +18,38 @@
 // per packed op; the half pairs hold elements (p, p+4) of an 8-element block,
 // and the activation tile in LDS is stored with the same in-block order.
 //
-// bf16 mode: activations are converted to fp16 when staged (exact for
-// |x| < 65504 away from fp16 subnormals) and each lane's 16-byte weight load
-// covers one scale group; the 4 matrix-core steps of a 128-wide K chunk take
-// one packed dword from each of the 4 groups, and A is read to match, so all
-// of K accumulates in one fp32 accumulator.
-// Exact mode: int8 activations are exact fp16 integers and each matrix-core
-// step covers exactly one scale group, so its result is s_w * G with G the
-// exact int32 group sum (every partial sum is an integer multiple of the
-// scale's last-bit weight below 2^24, hence exact in fp32); the group result is
-// folded into the row's accumulator as fma(s_w*G, s_x, acc), groups ascending.
+// Weights are read in a fragment-major layout made once by moe_int4_prepack
+// (an exact byte permutation of the checkpoint layout: int4 stays int4, the
+// scales stay bf16).  For expert e, 16-row group n16 and 128-wide K chunk c,
+// one 1 KB weight fragment holds, for lane l = r + 16 j, the 16 bytes
+// [dword of group 4c+g covering K 128c+32g+8j .. +7, g = 0..3] of row
+// 16 n16 + r; the matching 128-byte scale fragment holds the 4 group scales of
+// each of the 16 rows.  Each wave-wide load is then one contiguous 1 KB (or
+// 128 B) piece: every fetched cache line is used whole, at once.
+//
+// Each matrix-core step covers exactly one scale group (lane j supplies its
+// K sub-block j).  bf16 mode: activations are converted to fp16 (exact for
+// |x| < 65504 away from fp16 subnormals) and all of K accumulates in one fp32
+// accumulator.  Exact mode: int8 activations are exact fp16 integers, so a
+// step's result is s_w * G with G the exact int32 group sum (every partial sum
+// is an integer multiple of the scale's last-bit weight below 2^24, hence
+// exact in fp32); it is folded into the row's accumulator as
+// fma(s_w*G, s_x, acc), groups ascending.
 #include "moe_common.h"
 
 namespace {
 
 constexpr int kKC = 128;        // K elements per chunk (4 scale groups)
 constexpr int kAStride = 136;   // halves per LDS activation row (128 + 8 pad)
+constexpr int kFragBytes = 1024;  // weight fragment: 16 rows x 128 K
+constexpr int kFragScales = 64;   // scale fragment: 16 rows x 4 groups (bf16)
 
 struct GroupedArgs {
     const void* act;        // bf16 or int8 [rows][K]
     const float* act_scale; // exact: [rows][K/32]
-    const uint8_t* w0;      // gate (gate/up) or down
+    const uint8_t* w0;      // gate (gate/up) or down, prepacked
     const uint16_t* s0;
-    const uint8_t* w1;      // up (gate/up only)
+    const uint8_t* w1;      // up (gate/up only), prepacked
     const uint16_t* s1;
     const int32_t* offsets;
     const int32_t* sorted_slot;
@@ -97,6 +106,12 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bm, lo
         base += total;
     }
     return false;
+}
+
+// First fragment (chunk 0) of 16-row group n16 of expert e in a prepacked
+// matrix with N rows per expert and nch chunks per row.
+__device__ __forceinline__ size_t frag_index(int e, int n16, int N, int nch) {
+    return ((size_t)e * (size_t)(N / 16) + (size_t)n16) * (size_t)nch;
 }
 
 // 8 int4 weights of one packed dword (element p in nibble p) -> fp16 q*s,
@@ -192,29 +207,25 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
         rowsrc[tid] = src;
     }
 
-    // this wave's weight rows, per column block
-    const uint8_t* wrow[4];
-    const uint16_t* srow[4];
-    const size_t wmat = (size_t)N * (size_t)(K / 2);
-    const size_t smat = (size_t)N * (size_t)(K / 32);
+    // this wave's weight fragments, per column block (16 rows each)
+    const uint8_t* wf[4];
+    const uint16_t* sf[4];
     int n0;
     if (GATEUP) {
         n0 = nc * 128 + wave * 32;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            const int n = n0 + 16 * (cb & 1) + r;
-            const uint8_t* wb = (cb < 2 ? a.w0 : a.w1) + (size_t)ti.e * wmat;
-            const uint16_t* sb = (cb < 2 ? a.s0 : a.s1) + (size_t)ti.e * smat;
-            wrow[cb] = wb + (size_t)n * (K / 2);
-            srow[cb] = sb + (size_t)n * (K / 32);
+            const size_t f = frag_index(ti.e, (n0 >> 4) + (cb & 1), N, nch);
+            wf[cb] = (cb < 2 ? a.w0 : a.w1) + f * kFragBytes + lane * 16;
+            sf[cb] = (cb < 2 ? a.s0 : a.s1) + f * kFragScales + 4 * r;
         }
     } else {
         n0 = nc * 256 + wave * 64;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            const int n = n0 + 16 * cb + r;
-            wrow[cb] = a.w0 + (size_t)ti.e * wmat + (size_t)n * (K / 2);
-            srow[cb] = a.s0 + (size_t)ti.e * smat + (size_t)n * (K / 32);
+            const size_t f = frag_index(ti.e, (n0 >> 4) + cb, N, nch);
+            wf[cb] = a.w0 + f * kFragBytes + lane * 16;
+            sf[cb] = a.s0 + f * kFragScales + 4 * r;
         }
     }
     __syncthreads();  // rowsrc visible
@@ -222,25 +233,18 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     const int active_mb = (ti.rows + 15) >> 4;
 
     // ---- prefetch registers ----
-    u32x4_t Bq[4];       // bf16 mode: one 16-byte group per column block; exact: 4 dwords (groups 0..3)
-    uint32_t Sq[4][2];   // bf16 mode: Sq[cb][0] = scale bits; exact: 4 bf16 scales
+    u32x4_t Bq[4];       // dwords of groups 0..3 (K sub-block j), per column block
+    uint32_t Sq[4][2];   // 4 bf16 scales (groups 0..3) of the lane's row, per column block
     u32x4_t Aq[A_ITERS];
     f32x4_t SXq = {0.f, 0.f, 0.f, 0.f};
 
     auto load_B = [&](int c) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            if (!EXACT) {
-                Bq[cb] = *reinterpret_cast<const u32x4_t*>(wrow[cb] + (size_t)c * 64 + 16 * j);
-                Sq[cb][0] = srow[cb][c * 4 + j];
-            } else {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    Bq[cb][g] = *reinterpret_cast<const uint32_t*>(wrow[cb] + (size_t)c * 64 + 16 * g + 4 * j);
-                const u32x2_t s = *reinterpret_cast<const u32x2_t*>(srow[cb] + c * 4);
-                Sq[cb][0] = s[0];
-                Sq[cb][1] = s[1];
-            }
+            Bq[cb] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
+            const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
+            Sq[cb][0] = sv[0];
+            Sq[cb][1] = sv[1];
         }
     };
     auto load_A = [&](int c) {
@@ -311,18 +315,19 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
             load_A(c + 1);
         }
         if (!EXACT) {
-            half2_t s2[4], c2[4];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) scale_pair(Sc[cb][0], s2[cb], c2[cb]);
-#pragma unroll
-            for (int gp = 0; gp < 4; ++gp) {
+            for (int g = 0; g < 4; ++g) {
                 half8_t bf[4];
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) bf[cb] = dequant8(Bc[cb][gp], s2[cb], c2[cb]);
+                for (int cb = 0; cb < 4; ++cb) {
+                    half2_t s2, c2;
+                    scale_pair(Sc[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
+                    bf[cb] = dequant8(Bc[cb][g], s2, c2);
+                }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     if (mb < active_mb) {
-                        const half8_t af = *reinterpret_cast<const half8_t*>(&As[16 * mb + r][32 * j + 8 * gp]);
+                        const half8_t af = *reinterpret_cast<const half8_t*>(&As[16 * mb + r][32 * g + 8 * j]);
 #pragma unroll
                         for (int cb = 0; cb < 4; ++cb)
                             acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
@@ -419,27 +424,18 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
 }
 
 // Tiles of at most 16 rows (decode): the weights dominate the bytes, so each
-// wave streams its 64 weight rows independently with no workgroup barrier,
-// keeping the loads of the next two 128-wide K chunks in flight while it
-// converts and multiplies the current one.  The tile's activation rows (rows
-// past the tile's count read as zero) come straight from L2 in the MFMA
-// operand layout.
-//
-// Scales are staged in wave-private LDS per 1024-wide K block (32 scales = 64
-// bytes per row): each chunk also loads one eighth of the NEXT block's scale
-// rows as whole 64-byte segments, written to the other LDS buffer right after
-// the chunk is consumed.  Reading 2-8 scale bytes per row per chunk instead
-// would refetch each scale line from HBM many times (the scale rows of all
-// waves in flight outgrow the L2).  Every chunk issues the same unconditional
-// loads, so the outstanding-load counts stay exact.  Same arithmetic as k_grouped.
-constexpr int kSBlk = 8;        // chunks per scale block (32 scales per row)
-constexpr int kSStride = 36;    // halves per LDS scale row (32 + 4 pad)
-
-template <int MODE, int OP>
+// wave streams its 64 weight rows (4 fragments per chunk) independently, with
+// no workgroup barrier and no LDS.  Bytes in flight set the speed here: the
+// loads of the next D-1 chunks (weights, scales and the tile's activation rows)
+// are in flight while the current chunk is converted and multiplied.  Chunk
+// indices past the end are clamped (redundant in-bounds loads) rather than
+// skipped, so every step issues the same unconditional loads and the
+// outstanding-load counts stay exact; rows past the tile's count read row 0
+// and are zeroed at use.  Same arithmetic as k_grouped.
+template <int MODE, int OP, int D>
 __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
     constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
     constexpr bool GATEUP = OP == 0;
-    __shared__ __attribute__((aligned(16))) uint16_t Ssm[4][2][64][kSStride];
 
     const long L = xcd_logical_block(a.per_xcd);
     if (L >= a.n_logical) return;
@@ -455,7 +451,6 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
     const int K = a.K;
     const int N = a.N;
     const int nch = K / kKC;
-    const int srow_len = K / 32;  // scales per weight row (a multiple of 4)
 
     auto src_of = [&](int row) -> int {
         if (row >= ti.rows) return -1;
@@ -468,109 +463,73 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) dsrc[i] = EXACT ? src_of(4 * j + i) : -1;
 
-    // weight row of wave-local row index q (0..63): column block q/16, row q%16
-    const size_t wmat = (size_t)N * (size_t)(K / 2);
-    const size_t smat = (size_t)N * (size_t)(K / 32);
     const int n0 = GATEUP ? nc * 128 + wave * 32 : nc * 256 + wave * 64;
-    auto wrow_of = [&](int q) -> size_t {  // row index within its matrix
-        return GATEUP ? (size_t)(n0 + 16 * ((q >> 4) & 1) + (q & 15)) : (size_t)(n0 + q);
-    };
-    auto mat_of = [&](int q) -> int { return GATEUP ? (q >> 5) : 0; };  // 0 = w0/s0, 1 = w1/s1
-    const uint8_t* wrow[4];
+    const uint8_t* wf[4];
+    const uint16_t* sf[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-        const int q = 16 * cb + r;
-        wrow[cb] = (mat_of(q) ? a.w1 : a.w0) + (size_t)ti.e * wmat + wrow_of(q) * (K / 2);
+        const int n16 = (n0 >> 4) + (GATEUP ? (cb & 1) : cb);
+        const bool second = GATEUP && cb >= 2;
+        const size_t f = frag_index(ti.e, n16, N, nch);
+        wf[cb] = (second ? a.w1 : a.w0) + f * kFragBytes + lane * 16;
+        sf[cb] = (second ? a.s1 : a.s0) + f * kFragScales + 4 * r;
     }
-    // scale rows this lane stages: row 8*(c%8) + lane/8 of the wave's 64, 8 bytes at (lane%8)*8
-    auto srow_ptr = [&](int q) -> const uint16_t* {
-        return (mat_of(q) ? a.s1 : a.s0) + (size_t)ti.e * smat + wrow_of(q) * srow_len;
-    };
 
-    struct Chunk {
-        u32x4_t B[4];     // bf16 mode: one scale group per column block; exact: dwords of groups 0..3
-        u32x4_t A[4];     // bf16: 8 bf16 per MFMA step; exact: 8 int8 per group in A[g][0..1]
-        f32x4_t SX[4];    // exact: s_x of result rows 4j+i for groups 0..3
-        u32x2_t SN;       // 4 scales of the next scale block (one piece of one row)
+    struct Slot {
+        u32x4_t B[4];    // dwords of groups 0..3 (K sub-block j), per column block
+        u32x2_t S[4];    // 4 bf16 scales of the lane's row, per column block
+        u32x4_t A[4];    // per group: 8 bf16 (bf16 mode) or 8 int8 in A[g][0..1] (exact)
+        f32x4_t SX[4];   // exact: s_x of result rows 4j+i for groups 0..3
     };
-    auto load = [&](int c, Chunk& ch) {
+    auto load = [&](int c, Slot& sl) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            if (!EXACT) {
-                ch.B[cb] = *reinterpret_cast<const u32x4_t*>(wrow[cb] + (size_t)c * 64 + 16 * j);
-            } else {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    ch.B[cb][g] = *reinterpret_cast<const uint32_t*>(wrow[cb] + (size_t)c * 64 + 16 * g + 4 * j);
-            }
+            sl.B[cb] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
+            sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
         }
-        // rows past the tile read row 0 (zeroed at use): no load sits under a branch
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            u32x4_t v;
             if (!EXACT) {
-                v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + (size_t)arow * K +
-                                                       c * kKC + 32 * j + 8 * g);
+                sl.A[g] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + (size_t)arow * K +
+                                                             c * kKC + 32 * g + 8 * j);
             } else {
                 const u32x2_t q = *reinterpret_cast<const u32x2_t*>(static_cast<const int8_t*>(a.act) +
                                                                      (size_t)arow * K + c * kKC + 32 * g + 8 * j);
-                v = u32x4_t{q[0], q[1], 0u, 0u};
+                sl.A[g] = u32x4_t{q[0], q[1], 0u, 0u};
             }
-            ch.A[g] = v;
         }
         if (EXACT) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                ch.SX[i] = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)max(dsrc[i], 0) * (K / 32) + c * 4);
+                sl.SX[i] = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)max(dsrc[i], 0) * (K / 32) + c * 4);
         }
-        // next block's scales: row 8*(c%8) + lane/8, scales [32*(c/8+1) + 4*(lane%8), +4)
-        const int q = 8 * (c % kSBlk) + (lane >> 3);
-        const int sidx = 32 * (c / kSBlk + 1) + 4 * (lane & 7);
-        const int sclamp = sidx < srow_len ? sidx : 0;  // past the row: a valid address, never used
-        ch.SN = *reinterpret_cast<const u32x2_t*>(srow_ptr(q) + sclamp);
-    };
-    auto stage_next = [&](int c, const Chunk& ch) {  // after chunk c is consumed
-        const int q = 8 * (c % kSBlk) + (lane >> 3);
-        *reinterpret_cast<u32x2_t*>(&Ssm[wave][(c / kSBlk + 1) & 1][q][4 * (lane & 7)]) = ch.SN;
     };
 
     f32x4_t acc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int c, const Chunk& ch) {
-        const uint16_t(*sb)[kSStride] = Ssm[wave][(c / kSBlk) & 1];
-        const int cl = c % kSBlk;
-        if (!EXACT) {
-            half2_t s2[4], c2[4];
+    auto compute = [&](const Slot& sl) {
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) scale_pair(sb[16 * cb + r][4 * cl + j], s2[cb], c2[cb]);
+        for (int g = 0; g < 4; ++g) {
+            half8_t af;
+            f32x4_t sx;
+            if (!EXACT) {
+                af = __builtin_bit_cast(half8_t, bf16x8_to_f16_perm(avalid ? sl.A[g] : u32x4_t{0u, 0u, 0u, 0u}));
+            } else {
+                af = __builtin_bit_cast(half8_t, i8x8_to_f16_perm(avalid ? sl.A[g][0] : 0u, avalid ? sl.A[g][1] : 0u));
 #pragma unroll
-            for (int gp = 0; gp < 4; ++gp) {
-                const u32x4_t av = avalid ? ch.A[gp] : u32x4_t{0u, 0u, 0u, 0u};
-                const half8_t af = __builtin_bit_cast(half8_t, bf16x8_to_f16_perm(av));
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, dequant8(ch.B[cb][gp], s2[cb], c2[cb]),
-                                                                    acc[cb], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) sx[i] = dsrc[i] >= 0 ? sl.SX[i][g] : 0.0f;
             }
-        } else {
-            u32x2_t sv[4];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) sv[cb] = *reinterpret_cast<const u32x2_t*>(&sb[16 * cb + r][4 * cl]);
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x4_t a16 = i8x8_to_f16_perm(avalid ? ch.A[g][0] : 0u, avalid ? ch.A[g][1] : 0u);
-                const half8_t af = __builtin_bit_cast(half8_t, a16);
-                f32x4_t sx;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sx[i] = dsrc[i] >= 0 ? ch.SX[i][g] : 0.0f;
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    half2_t s2, c2;
-                    scale_pair(sv[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
-                    const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        af, dequant8(ch.B[cb][g], s2, c2), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            for (int cb = 0; cb < 4; ++cb) {
+                half2_t s2, c2;
+                scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
+                const half8_t bf = dequant8(sl.B[cb][g], s2, c2);
+                if (!EXACT) {
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[cb], 0, 0, 0);
+                } else {
+                    const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[cb][i] = __builtin_fmaf(d[i], sx[i], acc[cb][i]);
                 }
@@ -578,54 +537,24 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
         }
     };
 
-    // prologue: scale block 0 of all 64 rows, 8-byte pieces (4 scales; a row holds a
-    // multiple of 4 scales, so a piece lies wholly inside or wholly past its row)
+    // D chunk slots: chunk c+i lives in slot i of the iteration starting at c.
+    Slot sl[D];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int q = 8 * it + (lane >> 3);
-        const int sidx = 4 * (lane & 7);
-        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(srow_ptr(q) + (sidx < srow_len ? sidx : 0));
-        *reinterpret_cast<u32x2_t*>(&Ssm[wave][0][q][sidx]) = v;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-
-    // Three chunk slots: the two ahead are in flight while one is consumed.
-    // Chunk indices past the end are clamped (a redundant in-bounds load) rather
-    // than skipped, so no load sits under a branch; the scheduling barriers keep
-    // each chunk's loads where they are issued.
-    Chunk c0, c1, c2;
-    load(0, c0);
-    load(min(1, nch - 1), c1);
+    for (int i = 0; i < D - 1; ++i) load(min(i, nch - 1), sl[i]);
     __builtin_amdgcn_sched_barrier(0);
-    auto step = [&](int c, Chunk& cur, int cnext) {
-        compute(c, cur);
-        stage_next(c, cur);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        load(min(cnext, nch - 1), cur);
-        __builtin_amdgcn_sched_barrier(0);
-    };
     int c = 0;
-    for (; c + 3 <= nch; c += 3) {
-        load(min(c + 2, nch - 1), c2);
-        __builtin_amdgcn_sched_barrier(0);
-        step(c, c0, c + 3);
-        step(c + 1, c1, c + 4);
-        compute(c + 2, c2);
-        stage_next(c + 2, c2);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+    for (; c + D <= nch; c += D) {
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            load(min(c + i + D - 1, nch - 1), sl[(i + D - 1) % D]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(sl[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    if (c < nch) {
-        compute(c, c0);
-        stage_next(c, c0);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-    }
-    if (c + 1 < nch) compute(c + 1, c1);
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i)
+        if (c + i < nch) compute(sl[i]);
 
     // epilogue (rows 4j+i of the lane)
     if (GATEUP) {
@@ -677,6 +606,43 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
     }
 }
 
+// Checkpoint layout -> fragment layout.  One thread per 16-byte lane piece of
+// a weight fragment (fragment = (row group, chunk) in row-group-major order;
+// 16 row groups of consecutive rows per expert, experts consecutive).
+__global__ __launch_bounds__(256) void k_prepack_w(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                  long pieces, int K) {
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= pieces) return;
+    const int nch = K / kKC;
+    const int l = (int)(t & 63);
+    const long fid = t >> 6;
+    const long rg = fid / nch;
+    const int c = (int)(fid % nch);
+    const int r = l & 15, j = l >> 4;
+    const uint8_t* row = src + (size_t)(rg * 16 + r) * (size_t)(K / 2) + 64 * c + 4 * j;
+    u32x4_t v;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) v[g] = *reinterpret_cast<const uint32_t*>(row + 16 * g);
+    *reinterpret_cast<u32x4_t*>(dst + (size_t)t * 16) = v;
+}
+
+// One thread per (fragment, row): the row's 4 group scales of the chunk.
+__global__ __launch_bounds__(256) void k_prepack_s(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                  long pieces, int K) {
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= pieces) return;
+    const int nch = K / kKC;
+    const int r = (int)(t & 15);
+    const long fid = t >> 4;
+    const long rg = fid / nch;
+    const int c = (int)(fid % nch);
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src + (size_t)(rg * 16 + r) * (size_t)(K / 32) + 4 * c);
+    *reinterpret_cast<u32x2_t*>(dst + (size_t)t * 4) = v;
+}
+
+constexpr int kSkinnyDepth = 4;       // chunk slots of the decode kernel (D-1 chunks in flight)
+constexpr int kSkinnyDepthExact = 3;  // exact mode carries the activation scales too
+
 // Rows per tile: as many 16-row blocks as an average expert segment needs.
 int pick_mb(int S, int E) {
     const double avg = (double)S / (double)E;
@@ -695,7 +661,10 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
     a.per_xcd = moe::per_xcd(a.n_logical);
     const dim3 grid(8 * a.per_xcd), block(256);
     switch (mb) {
-    case 1: hipLaunchKernelGGL((k_grouped_skinny<MODE, OP>), grid, block, 0, st, a); break;
+    case 1:
+        hipLaunchKernelGGL((k_grouped_skinny<MODE, OP, MODE == MOE_MODE_EXACT_I8 ? kSkinnyDepthExact : kSkinnyDepth>),
+                           grid, block, 0, st, a);
+        break;
     case 2: hipLaunchKernelGGL((k_grouped<MODE, OP, 2>), grid, block, 0, st, a); break;
     case 4: hipLaunchKernelGGL((k_grouped<MODE, OP, 4>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((k_grouped<MODE, OP, 8>), grid, block, 0, st, a); break;
@@ -790,4 +759,29 @@ extern "C" int moe_int4_grouped_down(int mode, const void* h, const float* h_sca
     hipStream_t st = as_stream(stream);
     return exact ? launch_grouped<MOE_MODE_EXACT_I8, 1>(a, T * k, st, what)
                  : launch_grouped<MOE_MODE_BF16, 1>(a, T * k, st, what);
+}
+
+extern "C" int moe_int4_prepack(const uint8_t* packed, const uint16_t* scale, int E, int N, int K,
+                                uint8_t* packed_out, uint16_t* scale_out, void* stream) {
+    using namespace moe;
+    const char* what = "moe_int4_prepack";
+    if (E < 0 || N <= 0 || K <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes E=%d N=%d K=%d", what, E, N, K);
+    if (N % 16 != 0 || K % kKC != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d (multiple of 16) K=%d (multiple of 128)", what, N, K);
+    if (E == 0) return MOE_OK;
+    if (!packed || !scale || !packed_out || !scale_out) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    if (!aligned16(packed) || !aligned16(packed_out) || (reinterpret_cast<uintptr_t>(scale) & 7) ||
+        (reinterpret_cast<uintptr_t>(scale_out) & 7))
+        return fail(MOE_ERR_INVALID_ARG, "%s: packed buffers 16-byte, scale buffers 8-byte aligned", what);
+    const size_t wbytes = (size_t)E * N * (K / 2), sbytes = (size_t)E * N * (K / 32) * 2;
+    const uintptr_t pi = reinterpret_cast<uintptr_t>(packed), po = reinterpret_cast<uintptr_t>(packed_out);
+    const uintptr_t si = reinterpret_cast<uintptr_t>(scale), so = reinterpret_cast<uintptr_t>(scale_out);
+    if ((pi < po + wbytes && po < pi + wbytes) || (si < so + sbytes && so < si + sbytes))
+        return fail(MOE_ERR_INVALID_ARG, "%s: output overlaps input (the permutation is out of place)", what);
+    hipStream_t st = as_stream(stream);
+    const long wp = (long)(wbytes / 16), sp = (long)(sbytes / 8);
+    hipLaunchKernelGGL(k_prepack_w, dim3((unsigned)((wp + 255) / 256)), dim3(256), 0, st, packed, packed_out, wp, K);
+    if (int rc = launch_status(what)) return rc;
+    hipLaunchKernelGGL(k_prepack_s, dim3((unsigned)((sp + 255) / 256)), dim3(256), 0, st, scale, scale_out, sp, K);
+    return launch_status(what);
 }

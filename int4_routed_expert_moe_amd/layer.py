@@ -26,8 +26,22 @@ def _u8(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
+def prepack_experts(ex: dict) -> dict:
+    """Checkpoint-layout expert tensors (wg/sg, wu/su, wd/sd) -> the fragment layout
+    the grouped GEMMs read (one exact byte permutation per matrix, on the GPU)."""
+    out = {}
+    for w, s in (("wg", "sg"), ("wu", "su"), ("wd", "sd")):
+        pw, ps = torch.empty_like(ex[w]), torch.empty_like(ex[s])
+        _m.moe_int4_prepack(ex[w], ex[s], pw, ps)
+        out[w], out[s] = pw, ps
+    return out
+
+
 class MoELayer:
-    """Routed int4 experts + shared bf16 expert (+ optional K3 latent wrapper)."""
+    """Routed int4 experts + shared bf16 expert (+ optional K3 latent wrapper).
+
+    `experts` holds the routed weights in the checkpoint layout; they are
+    permuted once into the fragment layout here."""
 
     def __init__(self, cfg: dict, router_w, router_b, experts: dict, shared: dict | None = None,
                  latent: dict | None = None):
@@ -35,7 +49,7 @@ class MoELayer:
         self.mode = _m.MOE_MODE_EXACT_I8 if cfg["mode"] == "exact" else _m.MOE_MODE_BF16
         self.router_w = router_w
         self.router_b = router_b
-        self.ex = experts
+        self.ex = prepack_experts(experts)
         self.shared = shared
         self.latent = latent
         self.E, self.k, self.H, self.I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]

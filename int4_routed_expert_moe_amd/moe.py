@@ -42,6 +42,7 @@ EXPORTS = {
     "moe_route": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "moe_permute": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "moe_quant_act_int8": ([_P, _I, _I, _P, _P, _P], _I),
+    "moe_int4_prepack": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "moe_int4_grouped_swiglu": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_int4_grouped_down": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_I, _P, _P, _P, _P, _I, _I, _I, _P, _P], _I),
@@ -130,6 +131,21 @@ def moe_quant_act_int8(x, q, s):
     _need(q, torch.int8, (M, K), "q")
     _need(s, torch.float32, (M, K // 32), "s")
     _check("moe_quant_act_int8", _lib.moe_quant_act_int8(_ptr(x), M, K, _ptr(q), _ptr(s), _stream()))
+
+
+def moe_int4_prepack(packed, scale, packed_out, scale_out):
+    """Checkpoint-layout expert matrices [E, N, K/2] + [E, N, K/32] -> the fragment layout
+    the grouped GEMMs read (same shapes and dtypes, out of place)."""
+    if packed.dim() != 3:
+        raise ValueError("packed must be [E, N, K/2]")
+    E, N, K2 = packed.shape
+    K = 2 * K2
+    _need(packed, torch.uint8, (E, N, K // 2), "packed")
+    _need(scale, torch.bfloat16, (E, N, K // 32), "scale")
+    _need(packed_out, torch.uint8, (E, N, K // 2), "packed_out")
+    _need(scale_out, torch.bfloat16, (E, N, K // 32), "scale_out")
+    _check("moe_int4_prepack", _lib.moe_int4_prepack(_ptr(packed), _ptr(scale), E, N, K, _ptr(packed_out),
+                                                     _ptr(scale_out), _stream()))
 
 
 def moe_int4_grouped_swiglu(mode, act, act_scale, gate_packed, gate_scale, up_packed, up_scale, offsets,

@@ -100,4 +100,11 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.moe_dense_workspace_bytes(8192, 4096, 7168) == 0
     assert _status(lib, "moe_rmsnorm_bf16", fake, fake, ctypes.c_float(-1.0), fake, 4, 64, null) == -1
     assert _status(lib, "moe_int4_group_sums_i32", fake, fake, 20, 16, 64, fake, null) == -2
+    # prepack: N not a multiple of 16, K not a multiple of 128, overlapping output, misaligned scale
+    pp = "moe_int4_prepack"
+    assert _status(lib, pp, fake, fake, 2, 24, 256, P(0x100000), P(0x200000), null) == -2
+    assert _status(lib, pp, fake, fake, 2, 32, 200, P(0x100000), P(0x200000), null) == -2
+    assert _status(lib, pp, fake, fake, 2, 32, 256, fake, P(0x200000), null) == -1
+    assert _status(lib, pp, fake, P(0x3004), 2, 32, 256, P(0x100000), P(0x200000), null) == -1
+    assert _status(lib, pp, null, null, 0, 32, 256, null, null, null) == 0
     assert lib.moe_status_string(-3) == b"workspace missing or too small"

@@ -151,12 +151,42 @@ def _expert_set(g, E, H, I):
 
 
 def _dev_experts(W):
+    """Upload in the checkpoint layout and permute into the layout the grouped GEMMs read."""
+    from int4_routed_expert_moe_amd.layer import prepack_experts
     out = {}
     for n in ("wg", "wu", "wd"):
         out[n] = torch.from_numpy(W[n]).cuda()
     for n in ("sg", "su", "sd"):
         out[n] = bf16_dev(W[n])
-    return out
+    return prepack_experts(out)
+
+
+def _prepacked_ref(packed, scale):
+    """The fragment layout written out with numpy index arithmetic (row group R, chunk c,
+    lane l = r + 16 j, group g): the reading of the header's definition."""
+    E, N, K2 = packed.shape
+    K = 2 * K2
+    nch = K // 128
+    # packed[e, 16 R + r, 64 c + 16 g + 4 j + b] -> out[e, R, c, j, r, g, b]
+    w = packed.reshape(E, N // 16, 16, nch, 4, 4, 4)          # e, R, r, c, g, j, b
+    w = w.transpose(0, 1, 3, 5, 2, 4, 6)                      # e, R, c, j, r, g, b
+    s = scale.reshape(E, N // 16, 16, nch, 4).transpose(0, 1, 3, 2, 4)  # e, R, c, r, g
+    return np.ascontiguousarray(w).reshape(E, N, K2), np.ascontiguousarray(s).reshape(E, N, K // 32)
+
+
+@pytest.mark.parametrize("E,N,K,seed", [(3, 48, 256, 0), (2, 16, 128, 1), (1, 256, 7168, 2), (0, 32, 128, 3)])
+def test_prepack_layout_bitexact(m, E, N, K, seed):
+    say(f"prepack E={E} N={N} K={K}")
+    g = np.random.default_rng(seed)
+    packed = _packed(g, (E, N, K // 2))
+    scale = g.integers(0, 1 << 16, (E, N, K // 32), dtype=np.uint16)
+    pw = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    ps = torch.empty((E, N, K // 32), dtype=torch.bfloat16, device="cuda")
+    m.moe_int4_prepack(torch.from_numpy(packed).cuda(), bf16_dev(scale), pw, ps)
+    torch.cuda.synchronize()
+    rw, rs = _prepacked_ref(packed, scale)
+    np.testing.assert_array_equal(pw.cpu().numpy(), rw)
+    np.testing.assert_array_equal(np_bf16(ps), rs)
 
 
 def _routing(g, T, E, k, skew=False):
