@@ -58,8 +58,6 @@ struct GroupedArgs {
     int K;
     int N;          // output columns per matrix
     int n_chunks;   // column chunks per tile
-    long n_logical; // tile bound * n_chunks
-    int per_xcd;
     void* out;
     float* out_scale;
 };
@@ -70,42 +68,65 @@ struct TileInfo {
     int rows;   // rows in the tile (1..16*MB)
 };
 
-// Locate tile `tile` in the concatenation over experts of ceil(count_e / bm)
-// tiles each.  Every wave computes it; the result is wave-uniform.
-__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int bm, long tile,
-                          TileInfo& ti) {
+// Work items are (tile, column chunk) pairs: ceil(count_e / bm) tiles of up to
+// bm consecutive sorted rows per expert, n_chunks column chunks per tile.  The
+// grid is sized on the host for the worst case; here every wave derives the
+// real item count from the offsets (each lane owns a run of up to 16 experts,
+// so all offset loads are issued at once) and spreads the real items over the
+// 8 XCDs in equal contiguous runs (the items of one tile, which share its
+// activation rows, stay on one XCD).  Blocks past the real count return
+// false.  The result is wave-uniform.
+__device__ bool locate_item(const int32_t* __restrict__ offsets, int E, int bm, int n_chunks, TileInfo& ti,
+                            int& nc) {
     const int lane = lane_id();
-    long base = 0;
-    for (int c0 = 0; c0 < E; c0 += MOE_WAVE) {
-        const int e = c0 + lane;
-        int beg = 0, cnt = 0;
-        if (e < E) {
-            beg = offsets[e];
-            cnt = offsets[e + 1] - beg;
-        }
-        const int nt = (cnt + bm - 1) / bm;
-        int incl = nt;
+    const int per = (E + MOE_WAVE - 1) / MOE_WAVE;  // experts per lane (E <= 1024)
+    const int e0 = min(lane * per, E);
+    int bound[17];  // offsets[e0 .. e0+per], clamped to the last expert
 #pragma unroll
-        for (int d = 1; d < MOE_WAVE; d <<= 1) {
-            const int v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
-        }
-        const int total = __shfl(incl, MOE_WAVE - 1);
-        if (tile < base + total) {
-            const int excl = incl - nt;
-            const bool mine = (tile >= base + excl) && (tile < base + incl);
-            const uint64_t m = __ballot(mine);
-            const int src = __ffsll((unsigned long long)m) - 1;
-            const int j = (int)(tile - base - __shfl(excl, src));
-            const int sb = __shfl(beg, src), sc = __shfl(cnt, src);
-            ti.e = __shfl(e, src);
-            ti.row0 = sb + j * bm;
-            ti.rows = min(bm, sc - j * bm);
-            return true;
-        }
-        base += total;
+    for (int i = 0; i <= 16; ++i)
+        if (i <= per) bound[i] = offsets[min(e0 + i, E)];
+    int mine_tiles = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (i < per) mine_tiles += (bound[i + 1] - bound[i] + bm - 1) / bm;
+    int incl = mine_tiles;
+#pragma unroll
+    for (int d = 1; d < MOE_WAVE; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
     }
-    return false;
+    const long n_real = (long)__shfl(incl, MOE_WAVE - 1) * n_chunks;
+    const long per_xcd = (n_real + 7) / 8;
+    const long q = (long)(blockIdx.x >> 3);
+    if (q >= per_xcd) return false;
+    const long L = (long)(blockIdx.x & 7) * per_xcd + q;
+    if (L >= n_real) return false;
+    const long tile = L / n_chunks;
+    nc = (int)(L % n_chunks);
+    const int excl = incl - mine_tiles;
+    const uint64_t m = __ballot(tile >= excl && tile < incl);
+    const int src = __ffsll((unsigned long long)m) - 1;
+    int fe = 0, frow0 = 0, frows = 0;
+    if (lane == src) {
+        int t = (int)(tile - excl);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i < per && frows == 0) {
+                const int cnt = bound[i + 1] - bound[i];
+                const int nt = (cnt + bm - 1) / bm;
+                if (t < nt) {
+                    fe = e0 + i;
+                    frow0 = bound[i] + t * bm;
+                    frows = min(bm, cnt - t * bm);
+                }
+                t -= nt;
+            }
+        }
+    }
+    ti.e = __shfl(fe, src);
+    ti.row0 = __shfl(frow0, src);
+    ti.rows = __shfl(frows, src);
+    return true;
 }
 
 // First fragment (chunk 0) of 16-row group n16 of expert e in a prepacked
@@ -185,12 +206,9 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     __shared__ __attribute__((aligned(16))) float SX[EXACT ? 4 : 1][EXACT ? BM : 1];
     __shared__ int32_t rowsrc[BM];
 
-    const long L = xcd_logical_block(a.per_xcd);
-    if (L >= a.n_logical) return;
-    const long tile = L / a.n_chunks;
-    const int nc = (int)(L % a.n_chunks);
     TileInfo ti;
-    if (!find_tile(a.offsets, a.E, BM, tile, ti)) return;
+    int nc;
+    if (!locate_item(a.offsets, a.E, BM, a.n_chunks, ti, nc)) return;
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -437,12 +455,9 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
     constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
     constexpr bool GATEUP = OP == 0;
 
-    const long L = xcd_logical_block(a.per_xcd);
-    if (L >= a.n_logical) return;
-    const long tile = L / a.n_chunks;
-    const int nc = (int)(L % a.n_chunks);
     TileInfo ti;
-    if (!find_tile(a.offsets, a.E, 16, tile, ti)) return;
+    int nc;
+    if (!locate_item(a.offsets, a.E, 16, a.n_chunks, ti, nc)) return;
 
     const int lane = lane_id();
     const int wave = threadIdx.x >> 6;
@@ -657,9 +672,7 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
     const int mb = pick_mb(S, a.E);
     const int bm = 16 * mb;
     const long tiles = ((long)S + (long)a.E * (bm - 1)) / bm + 1;
-    a.n_logical = tiles * a.n_chunks;
-    a.per_xcd = moe::per_xcd(a.n_logical);
-    const dim3 grid(8 * a.per_xcd), block(256);
+    const dim3 grid(8 * moe::per_xcd(tiles * a.n_chunks)), block(256);
     switch (mb) {
     case 1:
         hipLaunchKernelGGL((k_grouped_skinny<MODE, OP, MODE == MOE_MODE_EXACT_I8 ? kSkinnyDepthExact : kSkinnyDepth>),
