@@ -5,7 +5,8 @@
  * call this file: only the tests, the smoke check and the CPU-baseline leg of
  * the benchmark use it.  It shares no code, header, table or constant with the
  * HIP library; every routine below is written from the pages' description of
- * the method (cited per function) and from the readings listed in the design doc.
+ * the method (cited per function); where the pages leave a step open, the
+ * reading taken is stated at the function.
  *
  * Conventions
  *   bf16 values travel as uint16_t bit patterns.
