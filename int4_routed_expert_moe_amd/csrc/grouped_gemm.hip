@@ -35,6 +35,8 @@
 // is an integer multiple of the scale's last-bit weight below 2^24, hence
 // exact in fp32); it is folded into the row's accumulator as
 // fma(s_w*G, s_x, acc), groups ascending.
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace {
@@ -68,8 +70,9 @@ struct TileInfo {
     int rows;   // rows in the tile (1..16*MB)
 };
 
-// Work items are (tile, column chunk) pairs: ceil(count_e / bm) tiles of up to
-// bm consecutive sorted rows per expert, n_chunks column chunks per tile.  The
+// Work items are (tile, column chunk) pairs: ceil(count_e / bm) tiles per expert
+// of ceil(count_e / tiles) consecutive sorted rows (the last may be shorter),
+// n_chunks column chunks per tile.  The
 // grid is sized on the host for the worst case; here every wave derives the
 // real item count from the offsets (each lane owns a run of up to 16 experts,
 // so all offset loads are issued at once) and spreads the real items over the
@@ -115,9 +118,10 @@ __device__ bool locate_item(const int32_t* __restrict__ offsets, int E, int bm, 
                 const int cnt = bound[i + 1] - bound[i];
                 const int nt = (cnt + bm - 1) / bm;
                 if (t < nt) {
+                    const int rpt = (cnt + nt - 1) / nt;  // balanced: the tiles differ by at most one row
                     fe = e0 + i;
-                    frow0 = bound[i] + t * bm;
-                    frows = min(bm, cnt - t * bm);
+                    frow0 = bound[i] + t * rpt;
+                    frows = min(rpt, cnt - t * rpt);
                 }
                 t -= nt;
             }
@@ -193,17 +197,36 @@ __device__ __forceinline__ u32x4_t i8x8_to_f16_perm(uint32_t d0, uint32_t d1) {
     return r;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt) but not for its global loads, so prefetched weights and the next
+// activation chunk stay in flight across it (a full __syncthreads also drains
+// every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Tiles of up to 16*MB rows (prefill and mid-size batches; MB = 2, 4, 6, 8, 12).  A workgroup is 4
+// waves; each wave owns 64 weight rows (4 fragments) and all tile rows, so a
+// dequantised weight fragment feeds up to MB matrix-core steps.  The tile's
+// activation rows are gathered, converted to fp16 and staged in LDS one
+// 128-wide K chunk ahead (double buffer, one LDS-only barrier per chunk);
+// weights and scales run two chunks ahead in a 3-slot register ring.  Rows
+// past the tile's count read a valid row and are never written out (an
+// output row depends only on its own activation row).
 template <int MODE, int OP, int MB>
 __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     constexpr int BM = 16 * MB;
     constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
     constexpr bool GATEUP = OP == 0;
-    // activation staging: bf16 rows are 16 pieces of 16 B per chunk, int8 rows 8
+    // activation staging: a bf16 row chunk is 16 pieces of 16 B, an int8 row chunk 8
     constexpr int PIECES = EXACT ? 8 : 16;
-    constexpr int A_ITERS = (BM * PIECES + 255) / 256;
+    constexpr int A_ITERS = BM * PIECES / 256;
+    static_assert(BM * PIECES % 256 == 0 && A_ITERS <= PIECES, "staging pieces must tile the workgroup");
 
-    __shared__ __attribute__((aligned(16))) _Float16 As[BM][kAStride];
-    __shared__ __attribute__((aligned(16))) float SX[EXACT ? 4 : 1][EXACT ? BM : 1];
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][kAStride];
+    __shared__ __attribute__((aligned(16))) float SXs[2][4][EXACT ? BM : 1];
     __shared__ int32_t rowsrc[BM];
 
     TileInfo ti;
@@ -228,83 +251,74 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     // this wave's weight fragments, per column block (16 rows each)
     const uint8_t* wf[4];
     const uint16_t* sf[4];
-    int n0;
-    if (GATEUP) {
-        n0 = nc * 128 + wave * 32;
+    const int n0 = GATEUP ? nc * 128 + wave * 32 : nc * 256 + wave * 64;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const size_t f = frag_index(ti.e, (n0 >> 4) + (cb & 1), N, nch);
-            wf[cb] = (cb < 2 ? a.w0 : a.w1) + f * kFragBytes + lane * 16;
-            sf[cb] = (cb < 2 ? a.s0 : a.s1) + f * kFragScales + 4 * r;
-        }
-    } else {
-        n0 = nc * 256 + wave * 64;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const size_t f = frag_index(ti.e, (n0 >> 4) + cb, N, nch);
-            wf[cb] = a.w0 + f * kFragBytes + lane * 16;
-            sf[cb] = a.s0 + f * kFragScales + 4 * r;
-        }
+    for (int cb = 0; cb < 4; ++cb) {
+        const int n16 = (n0 >> 4) + (GATEUP ? (cb & 1) : cb);
+        const bool second = GATEUP && cb >= 2;
+        const size_t f = frag_index(ti.e, n16, N, nch);
+        wf[cb] = (second ? a.w1 : a.w0) + f * kFragBytes + lane * 16;
+        sf[cb] = (second ? a.s1 : a.s0) + f * kFragScales + 4 * r;
     }
-    __syncthreads();  // rowsrc visible
+    lds_barrier();  // rowsrc visible
+
+    // staging: this thread moves the A_ITERS consecutive 16-byte pieces starting at
+    // piece tid*A_ITERS of the tile chunk (within one row, or across the end of one
+    // row into the next); rows past the tile take the tile's first row
+    constexpr int PIECE_ELEMS = EXACT ? 16 : 8;
+    const int lin0 = tid * A_ITERS;
+    const int srow = lin0 / PIECES;
+    const int spiece = lin0 % PIECES;
+    const int src0 = rowsrc[srow];
+    const int src1 = rowsrc[min(srow + 1, BM - 1)];
+    const int aoff0 = (src0 >= 0 ? src0 : rowsrc[0]) * K + spiece * PIECE_ELEMS;
+    const int aoff1 = (src1 >= 0 ? src1 : rowsrc[0]) * K - (PIECES - spiece) * PIECE_ELEMS;
+    auto piece_off = [&](int it) -> int { return (spiece + it < PIECES ? aoff0 : aoff1) + it * PIECE_ELEMS; };
+    int sxrow = 0;
+    if (EXACT && tid < BM) sxrow = rowsrc[tid] >= 0 ? rowsrc[tid] : rowsrc[0];
 
     const int active_mb = (ti.rows + 15) >> 4;
 
-    // ---- prefetch registers ----
-    u32x4_t Bq[4];       // dwords of groups 0..3 (K sub-block j), per column block
-    uint32_t Sq[4][2];   // 4 bf16 scales (groups 0..3) of the lane's row, per column block
-    u32x4_t Aq[A_ITERS];
-    f32x4_t SXq = {0.f, 0.f, 0.f, 0.f};
-
-    auto load_B = [&](int c) {
+    struct Slot {
+        u32x4_t B[4];   // dwords of groups 0..3 (K sub-block j), per column block
+        u32x2_t S[4];   // 4 bf16 scales of the lane's row, per column block
+    };
+    auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            Bq[cb] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
-            const u32x2_t sv = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
-            Sq[cb][0] = sv[0];
-            Sq[cb][1] = sv[1];
+            sl.B[cb] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
+            sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
         }
     };
-    auto load_A = [&](int c) {
+    u32x4_t Aq[A_ITERS];
+    f32x4_t SXq = {0.f, 0.f, 0.f, 0.f};
+    auto load_A = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
-            const int lin = it * 256 + tid;
-            const int row = lin / PIECES;
-            const int piece = lin % PIECES;
-            // rows past the tile load row 0 and are zeroed by a select (no load under a branch)
-            const int src = rowsrc[row < BM ? row : 0];
-            const int srow = (row < BM && src >= 0) ? src : 0;
-            u32x4_t v;
             if (!EXACT)
-                v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + (size_t)srow * K + c * kKC + piece * 8);
+                Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + piece_off(it) + c * kKC);
             else
-                v = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + (size_t)srow * K + c * kKC + piece * 16);
-            Aq[it] = (row < BM && src >= 0) ? v : u32x4_t{0u, 0u, 0u, 0u};
+                Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + piece_off(it) + c * kKC);
         }
-        if (EXACT) {
-            const int src = rowsrc[tid < BM ? tid : 0];
-            const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)max(src, 0) * (K / 32) + c * 4);
-            SXq = (tid < BM && src >= 0) ? sv : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        if (EXACT && tid < BM)
+            SXq = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)sxrow * (K / 32) + c * 4);
     };
-    auto store_A = [&]() {
+    auto store_A = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
-            const int lin = it * 256 + tid;
-            const int row = lin / PIECES;
-            const int piece = lin % PIECES;
-            if (row < BM) {
-                if (!EXACT) {
-                    *reinterpret_cast<u32x4_t*>(&As[row][piece * 8]) = bf16x8_to_f16_perm(Aq[it]);
-                } else {
-                    *reinterpret_cast<u32x4_t*>(&As[row][piece * 16]) = i8x8_to_f16_perm(Aq[it][0], Aq[it][1]);
-                    *reinterpret_cast<u32x4_t*>(&As[row][piece * 16 + 8]) = i8x8_to_f16_perm(Aq[it][2], Aq[it][3]);
-                }
+            const bool same = spiece + it < PIECES;
+            const int row = same ? srow : srow + 1;
+            const int piece = same ? spiece + it : spiece + it - PIECES;
+            if (!EXACT) {
+                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = bf16x8_to_f16_perm(Aq[it]);
+            } else {
+                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16]) = i8x8_to_f16_perm(Aq[it][0], Aq[it][1]);
+                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16 + 8]) = i8x8_to_f16_perm(Aq[it][2], Aq[it][3]);
             }
         }
         if (EXACT && tid < BM) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) SX[g][tid] = SXq[g];
+            for (int g = 0; g < 4; ++g) SXs[buf][g][tid] = SXq[g];
         }
     };
 
@@ -314,73 +328,113 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    load_B(0);
-    load_A(0);
-    store_A();
-    __syncthreads();
-
-    for (int c = 0; c < nch; ++c) {
-        u32x4_t Bc[4];
-        uint32_t Sc[4][2];
+    auto dequant_step = [&](const Slot& sl, int g, half8_t (&bf)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            Bc[cb] = Bq[cb];
-            Sc[cb][0] = Sq[cb][0];
-            Sc[cb][1] = Sq[cb][1];
+            half2_t s2, c2;
+            scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
+            bf[cb] = dequant8(sl.B[cb][g], s2, c2);
         }
-        if (c + 1 < nch) {
-            load_B(c + 1);
-            load_A(c + 1);
-        }
-        if (!EXACT) {
+    };
+    // NACT > 0 (bf16, tiles of 8 or more row blocks, sized so they run nearly
+    // full): all NACT row blocks with no branches, and the next step's
+    // dequantisation issued among the current step's matrix-core operations.
+    // NACT == 0: all MB row blocks, each under a uniform branch (keeps the
+    // register count of the smaller tiles within two waves per SIMD).
+    auto compute = [&](auto nact, int c, const Slot& sl) __attribute__((always_inline)) {
+        constexpr int NACT = decltype(nact)::value;
+        const int buf = c & 1;
+        if constexpr (NACT > 0) {
+            half8_t bfa[4], bfb[4];
+            dequant_step(sl, 0, bfa);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                half8_t bf[4];
+                half8_t(&cur)[4] = (g & 1) ? bfb : bfa;
+                half8_t(&nxt)[4] = (g & 1) ? bfa : bfb;
+                if (g < 3) dequant_step(sl, g + 1, nxt);
+                // fragment reads run two row blocks ahead; only VALU work (the
+                // dequantisation above) may move across row blocks
+                half8_t af0 = *reinterpret_cast<const half8_t*>(&As[buf][r][32 * g + 8 * j]);
+                half8_t af1 = *reinterpret_cast<const half8_t*>(&As[buf][16 + r][32 * g + 8 * j]);
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    half2_t s2, c2;
-                    scale_pair(Sc[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
-                    bf[cb] = dequant8(Bc[cb][g], s2, c2);
-                }
+                for (int mb = 0; mb < NACT; ++mb) {
+                    const half8_t af = af0;
+                    af0 = af1;
+                    if (mb + 2 < NACT)
+                        af1 = *reinterpret_cast<const half8_t*>(&As[buf][16 * (mb + 2) + r][32 * g + 8 * j]);
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    if (mb < active_mb) {
-                        const half8_t af = *reinterpret_cast<const half8_t*>(&As[16 * mb + r][32 * g + 8 * j]);
-#pragma unroll
-                        for (int cb = 0; cb < 4; ++cb)
-                            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
-                    }
+                    for (int cb = 0; cb < 4; ++cb)
+                        acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, cur[cb], acc[mb][cb], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0x0002);
                 }
             }
         } else {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 half8_t bf[4];
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    half2_t s2, c2;
-                    scale_pair(Sc[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
-                    bf[cb] = dequant8(Bc[cb][g], s2, c2);
-                }
+                dequant_step(sl, g, bf);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     if (mb < active_mb) {
-                        const half8_t af = *reinterpret_cast<const half8_t*>(&As[16 * mb + r][32 * g + 8 * j]);
-                        const f32x4_t sx = *reinterpret_cast<const f32x4_t*>(&SX[g][16 * mb + 4 * j]);
+                        const half8_t af = *reinterpret_cast<const half8_t*>(&As[buf][16 * mb + r][32 * g + 8 * j]);
+                        if (!EXACT) {
 #pragma unroll
-                        for (int cb = 0; cb < 4; ++cb) {
-                            const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                af, bf[cb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                            for (int cb = 0; cb < 4; ++cb)
+                                acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
+                        } else {
+                            const f32x4_t sx = *reinterpret_cast<const f32x4_t*>(&SXs[buf][g][16 * mb + 4 * j]);
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) acc[mb][cb][i] = __builtin_fmaf(d[i], sx[i], acc[mb][cb][i]);
+                            for (int cb = 0; cb < 4; ++cb) {
+                                const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    af, bf[cb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) acc[mb][cb][i] = __builtin_fmaf(d[i], sx[i], acc[mb][cb][i]);
+                            }
                         }
                     }
                 }
             }
         }
-        __syncthreads();
-        if (c + 1 < nch) store_A();
-        __syncthreads();
+    };
+
+    // prologue: weights of chunks 0..2 in flight, activation chunk 0 staged
+    Slot s0, s1, s2;
+    load_A(0);
+    load_B(0, s0);
+    load_B(min(1, nch - 1), s1);
+    load_B(min(2, nch - 1), s2);
+    store_A(0);
+    lds_barrier();
+
+    // One chunk: stage the next activation chunk's loads, multiply the current
+    // one, refill this weight slot three chunks ahead, then write the staged
+    // chunk to the other LDS buffer (whose last readers finished before the
+    // previous barrier).  Indices past the end are clamped: redundant in-bounds
+    // loads, and a staged buffer nobody reads.
+    auto main_loop = [&](auto nact) __attribute__((always_inline)) {
+        auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
+            load_A(min(c + 1, nch - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(nact, c, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            load_B(min(c + 3, nch - 1), cur);
+            __builtin_amdgcn_sched_barrier(0);
+            store_A((c + 1) & 1);
+            lds_barrier();
+        };
+        int c = 0;
+        for (; c + 3 <= nch; c += 3) {
+            step(c, s0);
+            step(c + 1, s1);
+            step(c + 2, s2);
+        }
+        if (c < nch) step(c, s0);
+        if (c + 1 < nch) step(c + 1, s1);
+    };
+    if constexpr (!EXACT && MB >= 8) {
+        main_loop(std::integral_constant<int, MB>{});
+    } else {
+        main_loop(std::integral_constant<int, 0>{});
     }
 
     // ---- epilogue ----
@@ -658,18 +712,23 @@ __global__ __launch_bounds__(256) void k_prepack_s(const uint16_t* __restrict__ 
 constexpr int kSkinnyDepth = 4;       // chunk slots of the decode kernel (D-1 chunks in flight)
 constexpr int kSkinnyDepthExact = 3;  // exact mode carries the activation scales too
 
-// Rows per tile: as many 16-row blocks as an average expert segment needs.
+// Rows per tile: the smallest tile that holds an average expert segment with
+// some margin (segments split into balanced tiles, so most tiles run full).
 int pick_mb(int S, int E) {
     const double avg = (double)S / (double)E;
     if (avg <= 12.0) return 1;
-    if (avg <= 24.0) return 2;
-    if (avg <= 48.0) return 4;
-    return 8;
+    const double need = 1.15 * avg;
+    if (need <= 32.0) return 2;
+    if (need <= 64.0) return 4;
+    if (need <= 96.0) return 6;
+    if (need <= 128.0) return 8;
+    return 12;
 }
 
 template <int MODE, int OP>
 int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
-    const int mb = pick_mb(S, a.E);
+    // exact mode carries a second product per step (s_w*G) and the s_x tile: at most 8 row blocks
+    const int mb = MODE == MOE_MODE_EXACT_I8 ? min(pick_mb(S, a.E), 8) : pick_mb(S, a.E);
     const int bm = 16 * mb;
     const long tiles = ((long)S + (long)a.E * (bm - 1)) / bm + 1;
     const dim3 grid(8 * moe::per_xcd(tiles * a.n_chunks)), block(256);
@@ -680,7 +739,9 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
         break;
     case 2: hipLaunchKernelGGL((k_grouped<MODE, OP, 2>), grid, block, 0, st, a); break;
     case 4: hipLaunchKernelGGL((k_grouped<MODE, OP, 4>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_grouped<MODE, OP, 8>), grid, block, 0, st, a); break;
+    case 6: hipLaunchKernelGGL((k_grouped<MODE, OP, 6>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_grouped<MODE, OP, 8>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_grouped<MODE, OP, MODE == MOE_MODE_EXACT_I8 ? 8 : 12>), grid, block, 0, st, a); break;
     }
     return moe::launch_status(what);
 }

@@ -206,6 +206,8 @@ def _routing(g, T, E, k, skew=False):
     (37, 512, 256, 8, 3, False, 1),      # ragged tail, one tile per expert
     (300, 256, 128, 4, 2, True, 2),      # many rows per expert (several tiles) and empty experts
     (700, 512, 256, 6, 2, False, 3),     # largest tile height
+    (280, 256, 128, 8, 2, False, 4),     # 6-block tiles
+    (400, 512, 256, 8, 2, True, 5),      # 8-block tiles, skewed
 ])
 def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     say(f"grouped bf16 T={T} H={H} I={I} E={E} k={k}")
@@ -236,13 +238,16 @@ def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     torch.cuda.synchronize()
     y_np = np_bf16(y)
     ref_out = oracle.combine_bf16(y_np[sp].reshape(T, k, H), w, shared)
-    assert_bf16_close(np_bf16(out), ref_out, "combine", atol_rms=1e-3, rtol=8e-3)
+    routed = oracle.combine_bf16(y_np[sp].reshape(T, k, H), w, None)  # bf16(sum) before the shared add
+    assert_bf16_close(np_bf16(out), ref_out, "combine", atol_rms=1e-3, rtol=8e-3, addends=(routed, shared))
 
 
 @pytest.mark.parametrize("T,H,I,E,k,skew,seed", [
     (64, 256, 128, 16, 2, False, 0),
     (300, 256, 128, 4, 2, True, 1),
     (45, 512, 256, 5, 3, False, 2),
+    (280, 256, 128, 8, 2, False, 3),     # 6-block tiles
+    (400, 512, 256, 8, 2, False, 4),     # 8-block tiles
 ])
 def test_grouped_exact_bitexact(m, T, H, I, E, k, skew, seed):
     say(f"grouped exact T={T} H={H} I={I} E={E} k={k}")
