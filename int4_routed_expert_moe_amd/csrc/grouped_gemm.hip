@@ -215,8 +215,10 @@ __device__ __forceinline__ void lds_barrier() {
 // weights and scales run two chunks ahead in a 3-slot register ring.  Rows
 // past the tile's count read a valid row and are never written out (an
 // output row depends only on its own activation row).
-template <int MODE, int OP, int MB>
+template <int MODE, int OP, int MB, int CB>
 __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
+    static_assert(CB == 2 || CB == 4, "column blocks per wave");
+    static_assert(CB == 4 || MODE == MOE_MODE_BF16, "exact mode quantises 32 output columns per wave");
     constexpr int BM = 16 * MB;
     constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
     constexpr bool GATEUP = OP == 0;
@@ -248,14 +250,16 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
         rowsrc[tid] = src;
     }
 
-    // this wave's weight fragments, per column block (16 rows each)
-    const uint8_t* wf[4];
-    const uint16_t* sf[4];
-    const int n0 = GATEUP ? nc * 128 + wave * 32 : nc * 256 + wave * 64;
+    // this wave's weight fragments, per column block (16 rows each): gate/up
+    // waves own 8*CB output columns (CB/2 gate blocks, then the matching up
+    // blocks), down waves 16*CB
+    const uint8_t* wf[CB];
+    const uint16_t* sf[CB];
+    const int n0 = GATEUP ? (nc * 4 + wave) * (8 * CB) : (nc * 4 + wave) * (16 * CB);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const int n16 = (n0 >> 4) + (GATEUP ? (cb & 1) : cb);
-        const bool second = GATEUP && cb >= 2;
+    for (int cb = 0; cb < CB; ++cb) {
+        const int n16 = (n0 >> 4) + (GATEUP ? (cb % (CB / 2)) : cb);
+        const bool second = GATEUP && cb >= CB / 2;
         const size_t f = frag_index(ti.e, n16, N, nch);
         wf[cb] = (second ? a.w1 : a.w0) + f * kFragBytes + lane * 16;
         sf[cb] = (second ? a.s1 : a.s0) + f * kFragScales + 4 * r;
@@ -280,12 +284,12 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     const int active_mb = (ti.rows + 15) >> 4;
 
     struct Slot {
-        u32x4_t B[4];   // dwords of groups 0..3 (K sub-block j), per column block
-        u32x2_t S[4];   // 4 bf16 scales of the lane's row, per column block
+        u32x4_t B[CB];   // dwords of groups 0..3 (K sub-block j), per column block
+        u32x2_t S[CB];   // 4 bf16 scales of the lane's row, per column block
     };
     auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < CB; ++cb) {
             sl.B[cb] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
             sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
         }
@@ -322,15 +326,15 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
         }
     };
 
-    f32x4_t acc[MB][4];
+    f32x4_t acc[MB][CB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < CB; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto dequant_step = [&](const Slot& sl, int g, half8_t (&bf)[4]) __attribute__((always_inline)) {
+    auto dequant_step = [&](const Slot& sl, int g, half8_t (&bf)[CB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < CB; ++cb) {
             half2_t s2, c2;
             scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
             bf[cb] = dequant8(sl.B[cb][g], s2, c2);
@@ -345,33 +349,35 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
         constexpr int NACT = decltype(nact)::value;
         const int buf = c & 1;
         if constexpr (NACT > 0) {
-            half8_t bfa[4], bfb[4];
+            // one stream of 4*NACT (group step, row block) products; fragment reads
+            // run PF products ahead, and only VALU work (the next group step's
+            // dequantisation) may move across products
+            constexpr int NS = 4 * NACT;
+            constexpr int PF = 4;
+            auto frag = [&](int st) __attribute__((always_inline)) {
+                return *reinterpret_cast<const half8_t*>(&As[buf][16 * (st % NACT) + r][32 * (st / NACT) + 8 * j]);
+            };
+            half8_t afr[NS];
+#pragma unroll
+            for (int q = 0; q < PF && q < NS; ++q) afr[q] = frag(q);
+            half8_t bfa[CB], bfb[CB];
             dequant_step(sl, 0, bfa);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                half8_t(&cur)[4] = (g & 1) ? bfb : bfa;
-                half8_t(&nxt)[4] = (g & 1) ? bfa : bfb;
-                if (g < 3) dequant_step(sl, g + 1, nxt);
-                // fragment reads run two row blocks ahead; only VALU work (the
-                // dequantisation above) may move across row blocks
-                half8_t af0 = *reinterpret_cast<const half8_t*>(&As[buf][r][32 * g + 8 * j]);
-                half8_t af1 = *reinterpret_cast<const half8_t*>(&As[buf][16 + r][32 * g + 8 * j]);
+            for (int st = 0; st < NS; ++st) {
+                const int g = st / NACT;
+                const int mb = st % NACT;
+                if (st + PF < NS) afr[st + PF] = frag(st + PF);
+                if (mb == 0 && g < 3) dequant_step(sl, g + 1, (g & 1) ? bfa : bfb);
+                half8_t(&cur)[CB] = (g & 1) ? bfb : bfa;
 #pragma unroll
-                for (int mb = 0; mb < NACT; ++mb) {
-                    const half8_t af = af0;
-                    af0 = af1;
-                    if (mb + 2 < NACT)
-                        af1 = *reinterpret_cast<const half8_t*>(&As[buf][16 * (mb + 2) + r][32 * g + 8 * j]);
-#pragma unroll
-                    for (int cb = 0; cb < 4; ++cb)
-                        acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, cur[cb], acc[mb][cb], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0x0002);
-                }
+                for (int cb = 0; cb < CB; ++cb)
+                    acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[st], cur[cb], acc[mb][cb], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0x0002);
             }
         } else {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                half8_t bf[4];
+                half8_t bf[CB];
                 dequant_step(sl, g, bf);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
@@ -379,12 +385,12 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
                         const half8_t af = *reinterpret_cast<const half8_t*>(&As[buf][16 * mb + r][32 * g + 8 * j]);
                         if (!EXACT) {
 #pragma unroll
-                            for (int cb = 0; cb < 4; ++cb)
+                            for (int cb = 0; cb < CB; ++cb)
                                 acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
                         } else {
                             const f32x4_t sx = *reinterpret_cast<const f32x4_t*>(&SXs[buf][g][16 * mb + 4 * j]);
 #pragma unroll
-                            for (int cb = 0; cb < 4; ++cb) {
+                            for (int cb = 0; cb < CB; ++cb) {
                                 const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                                     af, bf[cb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
@@ -450,16 +456,16 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
                 const size_t orow = (size_t)(ti.row0 + rl);
                 if (!EXACT) {
 #pragma unroll
-                    for (int p = 0; p < 2; ++p) {
+                    for (int p = 0; p < CB / 2; ++p) {
                         const uint32_t gb = f32_to_bf16_bits(acc[mb][p][i]);
-                        const uint32_t ub = f32_to_bf16_bits(acc[mb][2 + p][i]);
+                        const uint32_t ub = f32_to_bf16_bits(acc[mb][CB / 2 + p][i]);
                         const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
                         const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
                         if (ok) static_cast<uint16_t*>(a.out)[orow * N + n0 + 16 * p + r] = (uint16_t)hb;
                     }
                 } else {
-                    const float h0 = moe_silu(acc[mb][0][i]) * acc[mb][2][i];
-                    const float h1 = moe_silu(acc[mb][1][i]) * acc[mb][3][i];
+                    const float h0 = moe_silu(acc[mb][0][i]) * acc[mb][CB / 2][i];
+                    const float h1 = moe_silu(acc[mb][1][i]) * acc[mb][CB - 1][i];
                     float amax = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
                     for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
@@ -483,7 +489,7 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
                 if (rl >= ti.rows) continue;
                 const size_t orow = (size_t)(ti.row0 + rl);
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
+                for (int cb = 0; cb < CB; ++cb) {
                     const int col = n0 + 16 * cb + r;
                     if (!EXACT)
                         static_cast<uint16_t*>(a.out)[orow * N + col] = (uint16_t)f32_to_bf16_bits(acc[mb][cb][i]);
@@ -725,23 +731,38 @@ int pick_mb(int S, int E) {
     return 12;
 }
 
+// Column blocks per wave of the tile kernel: 2 for the 6- and 8-block bf16 tiles,
+// whose accumulators then leave room for more than one workgroup per CU; the
+// 12-block tiles keep 4 (halving them doubles the LDS fragment reads per product
+// and measured slower).
+constexpr int pick_cb(int mode, int mb) { return (mode == MOE_MODE_BF16 && mb >= 6 && mb < 12) ? 2 : 4; }
+
+template <int MODE, int OP, int MB, int CB>
+void launch_tiles(GroupedArgs a, int S, hipStream_t st) {
+    a.n_chunks = OP == 0 ? a.N / (32 * CB) : a.N / (64 * CB);
+    const long tiles = ((long)S + (long)a.E * (16 * MB - 1)) / (16 * MB) + 1;
+    hipLaunchKernelGGL((k_grouped<MODE, OP, MB, CB>), dim3(8 * moe::per_xcd(tiles * a.n_chunks)), dim3(256), 0, st,
+                       a);
+}
+
 template <int MODE, int OP>
 int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
     // exact mode carries a second product per step (s_w*G) and the s_x tile: at most 8 row blocks
-    const int mb = MODE == MOE_MODE_EXACT_I8 ? min(pick_mb(S, a.E), 8) : pick_mb(S, a.E);
-    const int bm = 16 * mb;
-    const long tiles = ((long)S + (long)a.E * (bm - 1)) / bm + 1;
-    const dim3 grid(8 * moe::per_xcd(tiles * a.n_chunks)), block(256);
+    constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
+    const int mb = EXACT ? min(pick_mb(S, a.E), 8) : pick_mb(S, a.E);
+    if (mb == 1) {
+        a.n_chunks = OP == 0 ? a.N / 128 : a.N / 256;
+        const long tiles = ((long)S + (long)a.E * 15) / 16 + 1;
+        hipLaunchKernelGGL((k_grouped_skinny<MODE, OP, EXACT ? kSkinnyDepthExact : kSkinnyDepth>),
+                           dim3(8 * moe::per_xcd(tiles * a.n_chunks)), dim3(256), 0, st, a);
+        return moe::launch_status(what);
+    }
     switch (mb) {
-    case 1:
-        hipLaunchKernelGGL((k_grouped_skinny<MODE, OP, MODE == MOE_MODE_EXACT_I8 ? kSkinnyDepthExact : kSkinnyDepth>),
-                           grid, block, 0, st, a);
-        break;
-    case 2: hipLaunchKernelGGL((k_grouped<MODE, OP, 2>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_grouped<MODE, OP, 4>), grid, block, 0, st, a); break;
-    case 6: hipLaunchKernelGGL((k_grouped<MODE, OP, 6>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_grouped<MODE, OP, 8>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_grouped<MODE, OP, MODE == MOE_MODE_EXACT_I8 ? 8 : 12>), grid, block, 0, st, a); break;
+    case 2: launch_tiles<MODE, OP, 2, pick_cb(MODE, 2)>(a, S, st); break;
+    case 4: launch_tiles<MODE, OP, 4, pick_cb(MODE, 4)>(a, S, st); break;
+    case 6: launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st); break;
+    case 8: launch_tiles<MODE, OP, 8, pick_cb(MODE, 8)>(a, S, st); break;
+    default: launch_tiles<MODE, OP, EXACT ? 8 : 12, pick_cb(MODE, EXACT ? 8 : 12)>(a, S, st); break;
     }
     return moe::launch_status(what);
 }
@@ -793,7 +814,6 @@ extern "C" int moe_int4_grouped_swiglu(int mode, const void* act, const float* a
     a.E = E;
     a.K = H;
     a.N = I;
-    a.n_chunks = I / 128;
     a.out = h;
     a.out_scale = h_scale;
     hipStream_t st = as_stream(stream);
@@ -828,7 +848,6 @@ extern "C" int moe_int4_grouped_down(int mode, const void* h, const float* h_sca
     a.E = E;
     a.K = I;
     a.N = H;
-    a.n_chunks = H / 256;
     a.out = y;
     hipStream_t st = as_stream(stream);
     return exact ? launch_grouped<MOE_MODE_EXACT_I8, 1>(a, T * k, st, what)
