@@ -12,9 +12,10 @@
 // layout of v_mfma_f32_16x16x32_bf16 (each lane holds 8 consecutive k of one
 // row / one weight row).  A workgroup of 4 waves stages a 16*MB-row A tile in
 // LDS per 128-wide K chunk; each wave streams its own 16*CB weight rows
-// straight from global memory (16 bytes per lane).  Decode-shaped problems
-// (few rows) split K over the grid and write fp32 partials that a second
-// kernel sums in a fixed order (deterministic), then applies the epilogue.
+// straight from global memory (16 bytes per lane) into a register ring.
+// Decode-shaped problems (few rows) split K over the grid and write fp32
+// partials that a second kernel sums in a fixed order (deterministic), then
+// applies the epilogue.
 #include "moe_common.h"
 
 namespace {
@@ -49,15 +50,26 @@ __device__ __forceinline__ uint32_t add_bits(uint32_t yb, uint16_t addv) {
     return f32_to_bf16_bits(bf16_bits_to_f32(yb) + bf16_bits_to_f32(addv));
 }
 
+// Workgroup barrier for LDS traffic only (waits for this wave's LDS operations,
+// not its global loads, so the weight prefetch survives it).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Column layout of a wave (CB blocks of 16 columns):
 //   linear: output columns n0 + 16 cb + r, n0 = chunk * 64 CB + wave * 16 CB
 //   swiglu: blocks [0, CB/2) gate, [CB/2, CB) up, same output columns
 //           n0 + 16 (cb mod CB/2) + r with n0 = chunk * 32 CB + wave * 8 CB
+// The A tile is double-buffered in LDS (one LDS-only barrier per chunk); each
+// wave's weight rows run D-1 chunks ahead in a ring of D register slots.
 template <int MB, int CB, int EPI, bool SPLIT>
 __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
     constexpr int BM = 16 * MB;
     constexpr int HALF = CB / 2;
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM][kDAStride];
+    constexpr int D = CB == 2 ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][kDAStride];
 
     const long L = xcd_logical_block(a.per_xcd);
     if (L >= a.n_logical) return;
@@ -77,48 +89,56 @@ __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
     const int nch = K / kDKC;
     const int c_beg = (int)((long)nch * ks / a.ksplit);
     const int c_end = (int)((long)nch * (ks + 1) / a.ksplit);
+    const int nloc = c_end - c_beg;  // >= 1 (the planner keeps at least two chunks per split)
 
+    // weight rows past N read the last row (never stored)
     int n0;
     const uint16_t* wrow[CB];
-    bool wave_on;
     if (EPI == EPI_SWIGLU) {
         n0 = nc * 32 * CB + wave * 8 * CB;
-        wave_on = n0 < a.N0;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             const int n = min(n0 + 16 * (cb % HALF) + r, a.N0 - 1);
-            wrow[cb] = (cb < HALF ? a.w0 : a.w1) + (size_t)n * K;
+            wrow[cb] = (cb < HALF ? a.w0 : a.w1) + (size_t)n * K + 8 * j;
         }
     } else {
         n0 = nc * 64 * CB + wave * 16 * CB;
-        wave_on = n0 < a.N0;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             const int n = min(n0 + 16 * cb + r, a.N0 - 1);
-            wrow[cb] = a.w0 + (size_t)n * K;
+            wrow[cb] = a.w0 + (size_t)n * K + 8 * j;
         }
     }
     const int active_mb = (rows + 15) >> 4;
 
-    constexpr int A_ITERS = (BM * 16 + 255) / 256;
+    // A staging: each thread moves A_ITERS 16-byte pieces of one row (rows past the
+    // tile read the tile's first row; their products are never stored)
+    constexpr int A_ITERS = BM * 16 / 256;
+    static_assert(BM * 16 % 256 == 0 && A_ITERS <= 16 && 16 % A_ITERS == 0, "A staging");
+    const int srow = (tid * A_ITERS) >> 4;
+    const int spiece = (tid * A_ITERS) & 15;
+    const uint16_t* aptr = a.x + (size_t)(m0 + (srow < rows ? srow : 0)) * K + spiece * 8;
     u32x4_t Aq[A_ITERS];
-    auto load_A = [&](int c) {
+    auto load_A = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < A_ITERS; ++it) {
-            const int lin = it * 256 + tid;
-            const int row = lin >> 4, piece = lin & 15;
-            // rows past the tile load the tile's first row and are zeroed by a select
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)(m0 + (row < rows ? row : 0)) * K + c * kDKC + piece * 8);
-            Aq[it] = row < rows ? v : u32x4_t{0u, 0u, 0u, 0u};
-        }
+        for (int it = 0; it < A_ITERS; ++it)
+            Aq[it] = *reinterpret_cast<const u32x4_t*>(aptr + (size_t)c * kDKC + 8 * it);
     };
-    auto store_A = [&]() {
+    auto store_A = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < A_ITERS; ++it) {
-            const int lin = it * 256 + tid;
-            const int row = lin >> 4, piece = lin & 15;
-            if (row < BM) *reinterpret_cast<u32x4_t*>(&As[row][piece * 8]) = Aq[it];
-        }
+        for (int it = 0; it < A_ITERS; ++it)
+            *reinterpret_cast<u32x4_t*>(&As[buf][srow][(spiece + it) * 8]) = Aq[it];
+    };
+
+    struct Slot {
+        u32x4_t B[CB][4];  // per column block and group step: 8 bf16 of the lane's weight row
+    };
+    auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                sl.B[cb][g] = *reinterpret_cast<const u32x4_t*>(wrow[cb] + (size_t)c * kDKC + 32 * g);
     };
 
     f32x4_t acc[MB][CB];
@@ -127,43 +147,56 @@ __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    load_A(c_beg);
-    store_A();
-    __syncthreads();
-    for (int c = c_beg; c < c_end; ++c) {
-        if (c + 1 < c_end) load_A(c + 1);
-        if (wave_on) {
+    auto compute = [&](int buf, const Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x8_t bfr[CB];
+        for (int g = 0; g < 4; ++g) {
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-                    bfr[cb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(
-                                                               wrow[cb] + c * kDKC + 32 * g + 8 * j));
+            for (int mb = 0; mb < MB; ++mb) {
+                if (mb < active_mb) {
+                    const bf16x8_t af = __builtin_bit_cast(
+                        bf16x8_t, *reinterpret_cast<const u32x4_t*>(&As[buf][16 * mb + r][32 * g + 8 * j]));
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    if (mb < active_mb) {
-                        const bf16x8_t af = __builtin_bit_cast(
-                            bf16x8_t, *reinterpret_cast<const u32x4_t*>(&As[16 * mb + r][32 * g + 8 * j]));
-#pragma unroll
-                        for (int cb = 0; cb < CB; ++cb)
-                            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[cb], acc[mb][cb], 0, 0, 0);
-                    }
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            af, __builtin_bit_cast(bf16x8_t, sl.B[cb][g]), acc[mb][cb], 0, 0, 0);
                 }
             }
         }
-        __syncthreads();
-        if (c + 1 < c_end) store_A();
-        __syncthreads();
+    };
+
+    // local chunk i = c_beg + i lives in slot i % D; indices past the split are
+    // clamped (redundant in-bounds loads, a staged buffer nobody reads)
+    Slot sl[D];
+    load_A(c_beg);
+#pragma unroll
+    for (int i = 0; i < D; ++i) load_B(c_beg + min(i, nloc - 1), sl[i]);
+    store_A(0);
+    lds_barrier();
+    auto step = [&](int i, Slot& cur) __attribute__((always_inline)) {
+        load_A(c_beg + min(i + 1, nloc - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i & 1, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        load_B(c_beg + min(i + D, nloc - 1), cur);
+        __builtin_amdgcn_sched_barrier(0);
+        store_A((i + 1) & 1);
+        lds_barrier();
+    };
+    int i = 0;
+    for (; i + D <= nloc; i += D) {
+#pragma unroll
+        for (int q = 0; q < D; ++q) step(i + q, sl[q]);
     }
-    if (!wave_on) return;
+#pragma unroll
+    for (int q = 0; q < D - 1; ++q)
+        if (i + q < nloc) step(i + q, sl[q]);
 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         if (mb >= active_mb) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rl = 16 * mb + 4 * j + i;
+        for (int ii = 0; ii < 4; ++ii) {
+            const int rl = 16 * mb + 4 * j + ii;
             if (rl >= rows) continue;
             const size_t m = (size_t)(m0 + rl);
             if (SPLIT) {
@@ -173,20 +206,20 @@ __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
                     int col;
                     if (EPI == EPI_SWIGLU) col = (cb < HALF ? 0 : a.N0) + n0 + 16 * (cb % HALF) + r;
                     else col = n0 + 16 * cb + r;
-                    if ((EPI == EPI_SWIGLU ? n0 + 16 * (cb % HALF) + r : col) < a.N0) prow[col] = acc[mb][cb][i];
+                    if ((EPI == EPI_SWIGLU ? n0 + 16 * (cb % HALF) + r : col) < a.N0) prow[col] = acc[mb][cb][ii];
                 }
             } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
                 for (int p = 0; p < HALF; ++p) {
                     const int col = n0 + 16 * p + r;
-                    if (col < a.N0) a.y[m * a.N0 + col] = (uint16_t)silu_mul_bits(acc[mb][p][i], acc[mb][HALF + p][i]);
+                    if (col < a.N0) a.y[m * a.N0 + col] = (uint16_t)silu_mul_bits(acc[mb][p][ii], acc[mb][HALF + p][ii]);
                 }
             } else {
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     const int col = n0 + 16 * cb + r;
                     if (col < a.N0) {
-                        uint32_t yb = f32_to_bf16_bits(acc[mb][cb][i]);
+                        uint32_t yb = f32_to_bf16_bits(acc[mb][cb][ii]);
                         if (a.add) yb = add_bits(yb, a.add[m * a.N0 + col]);
                         a.y[m * a.N0 + col] = (uint16_t)yb;
                     }
