@@ -13,123 +13,115 @@
 
 namespace {
 
-constexpr int kRouteTok = 64;   // tokens per block (one per lane)
-constexpr int kRouteKC = 64;    // hidden elements staged per LDS chunk
-constexpr int kRouteWaves = 4;
+constexpr int kRouteTok = 64;   // tokens per block
+constexpr int kRouteKC = 64;    // hidden elements per block sum (one LDS chunk)
 
-// Router rows bf16 -> fp32 (exact), so the logits kernel can read them as
-// wave-uniform scalar loads with no per-element conversion.
-__global__ __launch_bounds__(256) void k_router_w_f32(const uint16_t* __restrict__ w, long n,
-                                                      float* __restrict__ wf) {
-    const long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
-    if (i >= n) return;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(w + i);
-    f32x4_t lo, hi;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        lo[2 * j] = __uint_as_float(v[j] << 16);
-        lo[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
-        hi[2 * j] = __uint_as_float(v[2 + j] << 16);
-        hi[2 * j + 1] = __uint_as_float(v[2 + j] & 0xFFFF0000u);
-    }
-    *reinterpret_cast<f32x4_t*>(wf + i) = lo;
-    *reinterpret_cast<f32x4_t*>(wf + i + 4) = hi;
+// Workgroup barrier for LDS traffic only (the next tiles' global loads stay in
+// flight across it).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Logits of 64 tokens x (4 * EPW) experts.  Lanes are tokens; wave w runs the
-// EPW chains of experts eb + w*EPW + q side by side.  The x tile of each
-// 64-wide hidden chunk is staged in LDS as fp32, double buffered (the loads of
-// chunk c+1 are in flight while chunk c is consumed; one barrier per chunk);
-// the fp32 router rows are wave-uniform and come through the scalar cache.
-// Each chain adds its products in ascending hidden index, one fused
-// multiply-add per element (the product of two bf16 values is exact in fp32,
-// so this equals a multiply then an add).
-template <int EPW>
-__global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x,
-                                                       const float* __restrict__ wf, int T, int H,
-                                                       int E, float* __restrict__ logits) {
-    constexpr int XPIECES = kRouteTok * (kRouteKC / 8);  // 16-byte pieces of the x tile
-    constexpr int XITER = XPIECES / 256;
-    __shared__ __attribute__((aligned(16))) float xs[2][kRouteTok][kRouteKC + 4];
+// Stage 64 rows x 64 hidden elements of a bf16 matrix as fp32, transposed to
+// [i][row]; rows at or past `limit` are zero.  Two 16-byte pieces per thread.
+struct TileLoad {
+    u32x4_t v[2];
+};
+__device__ __forceinline__ void tile_load(TileLoad& tl, const uint16_t* __restrict__ m, int row0, int limit, int H,
+                                          int col0) {
     const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int wave = tid >> 6;
-    const int t0 = blockIdx.x * kRouteTok;
-    const int e0 = __builtin_amdgcn_readfirstlane((int)((blockIdx.y * kRouteWaves + wave) * EPW));
-
-    const float* wq[EPW];
 #pragma unroll
-    for (int q = 0; q < EPW; ++q) wq[q] = wf + (size_t)min(e0 + q, E - 1) * H;  // rows past E: never stored
-
-    u32x4_t xq[XITER];
-    auto load = [&](int c) {
-#pragma unroll
-        for (int it = 0; it < XITER; ++it) {
-            const int p = it * 256 + tid;
-            const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
-            // rows past T load row 0 and are zeroed by a select (no load under a branch)
-            const bool ok = t0 + row < T;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (size_t)(ok ? t0 + row : 0) * H + c + piece * 8);
-            xq[it] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < XITER; ++it) {
-            const int p = it * 256 + tid;
-            const int row = p / (kRouteKC / 8), piece = p % (kRouteKC / 8);
-            f32x4_t lo, hi;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                lo[2 * j] = __uint_as_float(xq[it][j] << 16);
-                lo[2 * j + 1] = __uint_as_float(xq[it][j] & 0xFFFF0000u);
-                hi[2 * j] = __uint_as_float(xq[it][2 + j] << 16);
-                hi[2 * j + 1] = __uint_as_float(xq[it][2 + j] & 0xFFFF0000u);
-            }
-            *reinterpret_cast<f32x4_t*>(&xs[buf][row][piece * 8]) = lo;
-            *reinterpret_cast<f32x4_t*>(&xs[buf][row][piece * 8 + 4]) = hi;
-        }
-    };
-
-    float acc[EPW], total[EPW];
-#pragma unroll
-    for (int q = 0; q < EPW; ++q) total[q] = 0.0f;
-    const int nch = H / kRouteKC;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < nch) load((c + 1) * kRouteKC);
-        const int cbase = c * kRouteKC;
-#pragma unroll
-        for (int q = 0; q < EPW; ++q) acc[q] = 0.0f;
-#pragma unroll 2
-        for (int i = 0; i < kRouteKC; i += 4) {
-            const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[buf][lane][i]);
-#pragma unroll
-            for (int q = 0; q < EPW; ++q) {
-                const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(wq[q] + cbase + i);
-                float a = acc[q];
-                a = __builtin_fmaf(xv[0], wv[0], a);
-                a = __builtin_fmaf(xv[1], wv[1], a);
-                a = __builtin_fmaf(xv[2], wv[2], a);
-                a = __builtin_fmaf(xv[3], wv[3], a);
-                acc[q] = a;
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < EPW; ++q) total[q] = total[q] + acc[q];  // block sums in ascending order
-        if (c + 1 < nch) store(buf ^ 1);
-        __syncthreads();
+    for (int it = 0; it < 2; ++it) {
+        const int p = it * 256 + tid;  // 512 pieces of 8 elements
+        const int row = p >> 3, piece = p & 7;
+        const bool ok = row0 + row < limit;
+        tl.v[it] = *reinterpret_cast<const u32x4_t*>(m + (size_t)(ok ? row0 + row : 0) * H + col0 + piece * 8);
+        if (!ok) tl.v[it] = u32x4_t{0u, 0u, 0u, 0u};
     }
-    const int t = t0 + lane;
-    if (t < T) {
+}
+__device__ __forceinline__ void tile_store(const TileLoad& tl, float (*dst)[64 + 4]) {
+    const int tid = threadIdx.x;
 #pragma unroll
-        for (int q = 0; q < EPW; ++q) {
-            const int e = e0 + q;
-            if (e < E) logits[(size_t)t * E + e] = total[q];
+    for (int it = 0; it < 2; ++it) {
+        const int p = it * 256 + tid;
+        const int row = p >> 3, piece = p & 7;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dst[piece * 8 + 2 * j][row] = __uint_as_float(tl.v[it][j] << 16);
+            dst[piece * 8 + 2 * j + 1][row] = __uint_as_float(tl.v[it][j] & 0xFFFF0000u);
         }
+    }
+}
+
+// One 64-long ascending chain per (token, expert) of a 4x4 register tile.
+__device__ __forceinline__ void block_chain(const float (*xs)[64 + 4], const float (*ws)[64 + 4], int tt, int te,
+                                            float (&acc)[4][4]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < kRouteKC; ++i) {
+        const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[i][4 * tt]);
+        const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(&ws[i][4 * te]);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[a][c] = __builtin_fmaf(xv[a], wv[c], acc[a][c]);
+    }
+}
+
+// Logits of 64 tokens x 64 experts for many tokens: each thread owns 4 tokens x
+// 4 experts; per 64-wide hidden block it forms the block sums (ascending chain)
+// and adds them to its running totals in ascending block order.  x and router
+// tiles are staged in LDS as fp32, double buffered: the next block's loads are
+// in flight during the current block's chains (one LDS-only barrier per block).
+// Grid: (ceil(E/64), ceil(T/64)).
+__global__ __launch_bounds__(256) void k_router_full(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                     int T, int H, int E, float* __restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) float xs[2][kRouteKC][64 + 4];  // [i][t]
+    __shared__ __attribute__((aligned(16))) float ws[2][kRouteKC][64 + 4];  // [i][e]
+    const int tid = threadIdx.x;
+    const int e0 = blockIdx.x * 64;
+    const int t0 = blockIdx.y * kRouteTok;
+    const int NB = H / kRouteKC;
+    const int tt = tid >> 4, te = tid & 15;
+    TileLoad lx, lw;
+    tile_load(lx, x, t0, T, H, 0);
+    tile_load(lw, w, e0, E, H, 0);
+    tile_store(lx, xs[0]);
+    tile_store(lw, ws[0]);
+    lds_barrier();
+    float total[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) total[a][c] = 0.0f;
+    for (int b = 0; b < NB; ++b) {
+        const int buf = b & 1;
+        const int bn = min(b + 1, NB - 1);  // past the end: a redundant in-bounds load, never used
+        tile_load(lx, x, t0, T, H, bn * kRouteKC);
+        tile_load(lw, w, e0, E, H, bn * kRouteKC);
+        float acc[4][4];
+        block_chain(xs[buf], ws[buf], tt, te, acc);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) total[a][c] = total[a][c] + acc[a][c];  // block sums in ascending order
+        tile_store(lx, xs[buf ^ 1]);
+        tile_store(lw, ws[buf ^ 1]);
+        lds_barrier();
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int t = t0 + 4 * tt + a;
+        if (t >= T) continue;
+        float* dst = logits + (size_t)t * E + e0 + 4 * te;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (e0 + 4 * te + c < E) dst[c] = total[a][c];
     }
 }
 
@@ -148,38 +140,15 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     const int e0 = blockIdx.y * 64;
     const int t0 = blockIdx.z * 64;
     const int NB = H / kRouteKC;
-    // stage: 64 rows x 64 elements of x and of w, transposed to [i][row]
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int p = it * 256 + tid;          // 512 pieces of 8 elements per matrix
-        const int row = p >> 3, piece = p & 7;
-        const bool okx = t0 + row < T, okw = e0 + row < E;
-        const u32x4_t vx = *reinterpret_cast<const u32x4_t*>(x + (size_t)(okx ? t0 + row : 0) * H + b * kRouteKC + piece * 8);
-        const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(w + (size_t)(okw ? e0 + row : 0) * H + b * kRouteKC + piece * 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            xs[piece * 8 + 2 * j][row] = okx ? __uint_as_float(vx[j] << 16) : 0.0f;
-            xs[piece * 8 + 2 * j + 1][row] = okx ? __uint_as_float(vx[j] & 0xFFFF0000u) : 0.0f;
-            ws[piece * 8 + 2 * j][row] = okw ? __uint_as_float(vw[j] << 16) : 0.0f;
-            ws[piece * 8 + 2 * j + 1][row] = okw ? __uint_as_float(vw[j] & 0xFFFF0000u) : 0.0f;
-        }
-    }
+    TileLoad lx, lw;
+    tile_load(lx, x, t0, T, H, b * kRouteKC);
+    tile_load(lw, w, e0, E, H, b * kRouteKC);
+    tile_store(lx, xs);
+    tile_store(lw, ws);
     __syncthreads();
     const int tt = tid >> 4, te = tid & 15;
     float acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = 0.0f;
-#pragma unroll 4
-    for (int i = 0; i < kRouteKC; ++i) {
-        const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[i][4 * tt]);
-        const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(&ws[i][4 * te]);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[a][c] = __builtin_fmaf(xv[a], wv[c], acc[a][c]);
-    }
+    block_chain(xs, ws, tt, te, acc);
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int t = t0 + 4 * tt + a;
@@ -300,14 +269,11 @@ constexpr int kPartialsMaxT = 256;
 
 }  // namespace
 
-// Few tokens: block sums [T, H/64, E] fp32.  Many tokens: logits [T, E] fp32,
-// then the fp32 router rows [E, H] (256-byte aligned).
-static size_t logits_bytes(int T, int E) { return (((size_t)T * (size_t)E * sizeof(float)) + 255) & ~(size_t)255; }
-
+// Few tokens: block sums [T, H/64, E] fp32.  Many tokens: logits [T, E] fp32.
 extern "C" size_t moe_route_workspace_bytes(int T, int H, int E) {
     if (T <= 0 || E <= 0 || H <= 0) return 0;
     if (T <= kPartialsMaxT) return (size_t)T * (size_t)(H / kRouteKC) * (size_t)E * sizeof(float);
-    return logits_bytes(T, E) + (size_t)E * (size_t)H * sizeof(float);
+    return (size_t)T * (size_t)E * sizeof(float);
 }
 
 extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
@@ -338,11 +304,7 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const floa
         dim3 grid(nb, (E + 63) / 64, tb);
         hipLaunchKernelGGL(k_router_partials, grid, dim3(256), 0, st, x, w_router, T, H, E, logits);
     } else {
-        float* wf = reinterpret_cast<float*>(static_cast<char*>(ws) + logits_bytes(T, E));
-        const long nw = (long)E * H;
-        hipLaunchKernelGGL(k_router_w_f32, dim3((unsigned)((nw / 8 + 255) / 256)), dim3(256), 0, st, w_router, nw, wf);
-        dim3 grid(tb, (E + kRouteWaves * 8 - 1) / (kRouteWaves * 8));
-        hipLaunchKernelGGL(k_router_logits<8>, grid, dim3(256), 0, st, x, wf, T, H, E, logits);
+        hipLaunchKernelGGL(k_router_full, dim3((E + 63) / 64, tb), dim3(256), 0, st, x, w_router, T, H, E, logits);
     }
     int rc = launch_status("moe_route logits");
     if (rc) return rc;
