@@ -344,7 +344,7 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     // full): all NACT row blocks with no branches, and the next step's
     // dequantisation issued among the current step's matrix-core operations.
     // NACT == 0: all MB row blocks, each under a uniform branch (keeps the
-    // register count of the smaller tiles within two waves per SIMD).
+    // register count of the smaller tiles, and of exact mode, in bounds).
     auto compute = [&](auto nact, int c, const Slot& sl) __attribute__((always_inline)) {
         constexpr int NACT = decltype(nact)::value;
         const int buf = c & 1;
@@ -747,9 +747,10 @@ void launch_tiles(GroupedArgs a, int S, hipStream_t st) {
 
 template <int MODE, int OP>
 int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
-    // exact mode carries a second product per step (s_w*G) and the s_x tile: at most 8 row blocks
+    // exact mode keeps its accumulators in VGPRs (the group folds are VALU work)
+    // and carries the s_x tile: at most 4 row blocks
     constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
-    const int mb = EXACT ? min(pick_mb(S, a.E), 8) : pick_mb(S, a.E);
+    const int mb = EXACT ? min(pick_mb(S, a.E), 4) : pick_mb(S, a.E);
     if (mb == 1) {
         a.n_chunks = OP == 0 ? a.N / 128 : a.N / 256;
         const long tiles = ((long)S + (long)a.E * 15) / 16 + 1;
@@ -757,12 +758,17 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
                            dim3(8 * moe::per_xcd(tiles * a.n_chunks)), dim3(256), 0, st, a);
         return moe::launch_status(what);
     }
-    switch (mb) {
-    case 2: launch_tiles<MODE, OP, 2, pick_cb(MODE, 2)>(a, S, st); break;
-    case 4: launch_tiles<MODE, OP, 4, pick_cb(MODE, 4)>(a, S, st); break;
-    case 6: launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st); break;
-    case 8: launch_tiles<MODE, OP, 8, pick_cb(MODE, 8)>(a, S, st); break;
-    default: launch_tiles<MODE, OP, EXACT ? 8 : 12, pick_cb(MODE, EXACT ? 8 : 12)>(a, S, st); break;
+    if constexpr (EXACT) {
+        if (mb == 2) launch_tiles<MODE, OP, 2, 4>(a, S, st);
+        else launch_tiles<MODE, OP, 4, 4>(a, S, st);
+    } else {
+        switch (mb) {
+        case 2: launch_tiles<MODE, OP, 2, pick_cb(MODE, 2)>(a, S, st); break;
+        case 4: launch_tiles<MODE, OP, 4, pick_cb(MODE, 4)>(a, S, st); break;
+        case 6: launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st); break;
+        case 8: launch_tiles<MODE, OP, 8, pick_cb(MODE, 8)>(a, S, st); break;
+        default: launch_tiles<MODE, OP, 12, pick_cb(MODE, 12)>(a, S, st); break;
+        }
     }
     return moe::launch_status(what);
 }
