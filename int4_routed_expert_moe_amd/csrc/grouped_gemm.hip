@@ -501,6 +501,194 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     }
 }
 
+// Large bf16 tiles on the 32x32x16 matrix-core shape (one wave per SIMD drives
+// it at close to the peak rate; the 16x16x32 shape needs two).  Tiles of
+// 32*M32 rows; each wave owns two 32-row column blocks (gate/up: 32 gate rows
+// and the matching 32 up rows; down: 64 output columns) and all tile rows.
+// Operands: lane l = c + 32 kb holds row/column c of a 32-block and K
+// sub-block kb of each 16-wide K step.  From the fragment layout a lane takes
+// the 16-byte pieces of 16-row lanes (c mod 16, kb) and (c mod 16, kb + 2):
+// dword g of the first holds K step 2g, of the second step 2g + 1.  The
+// accumulator element i of lane l is row 8(i/4) + 4 kb + i%4, column c.
+// Staging, barrier and weight ring as in k_grouped.
+template <int OP, int M32>
+__global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
+    constexpr int BM = 32 * M32;
+    constexpr bool GATEUP = OP == 0;
+    constexpr int PIECES = 16;
+    constexpr int A_ITERS = BM * PIECES / 256;
+    constexpr int AST = 144;  // halves per LDS row (128 + 16 pad)
+    static_assert(BM % 16 == 0 && A_ITERS * 4 * 4 == BM, "staging: 4 rows per wave instruction");
+
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][AST];
+    __shared__ int32_t rowsrc[BM];
+
+    TileInfo ti;
+    int nc;
+    if (!locate_item(a.offsets, a.E, BM, a.n_chunks, ti, nc)) return;
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int c32 = lane & 31;  // row (A) / column (B, D) within a 32-block
+    const int kb = lane >> 5;   // K sub-block within a 16-wide step
+    const int K = a.K;
+    const int N = a.N;
+    const int nch = K / kKC;
+
+    if (tid < BM) {
+        int src = -1;
+        if (tid < ti.rows) src = GATEUP ? a.sorted_slot[ti.row0 + tid] / a.k : ti.row0 + tid;
+        rowsrc[tid] = src;
+    }
+
+    // this wave's two 32-row column blocks: first 16-row group of each, its fragment pointers
+    const int n0 = GATEUP ? (nc * 4 + wave) * 32 : (nc * 4 + wave) * 64;
+    const uint8_t* wf[2];
+    const uint16_t* sf[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int n16 = (GATEUP ? n0 : n0 + 32 * cb) / 16 + (c32 >> 4);
+        const bool second = GATEUP && cb == 1;
+        const size_t f = frag_index(ti.e, n16, N, nch);
+        wf[cb] = (second ? a.w1 : a.w0) + f * kFragBytes + ((c32 & 15) + 16 * kb) * 16;
+        sf[cb] = (second ? a.s1 : a.s0) + f * kFragScales + 4 * (c32 & 15);
+    }
+    lds_barrier();  // rowsrc visible
+
+    // staging: each load instruction of a wave reads 4 whole row chunks (16 lanes x
+    // 16 contiguous bytes per row), so every cache line it touches is used whole;
+    // wave w moves rows A_ITERS*4*w + 4*it + lane/16.  Rows past the tile take the
+    // tile's first row.
+    int aoff[A_ITERS];
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) {
+        const int src = rowsrc[A_ITERS * 4 * wave + 4 * it + (lane >> 4)];
+        aoff[it] = (src >= 0 ? src : rowsrc[0]) * K + (lane & 15) * 8;
+    }
+
+    struct Slot {
+        u32x4_t B[2][2];  // per column block: pieces (kb) and (kb + 2)
+        u32x2_t S[2];     // per column block: 4 bf16 group scales of the lane's column
+    };
+    auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            sl.B[cb][0] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
+            sl.B[cb][1] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes + 512);
+            sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
+        }
+    };
+    u32x4_t Aq[A_ITERS];
+    auto load_A = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it)
+            Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + aoff[it] + c * kKC);
+    };
+    auto store_A = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it)
+            *reinterpret_cast<u32x4_t*>(&As[buf][A_ITERS * 4 * wave + 4 * it + (lane >> 4)][(lane & 15) * 8]) =
+                bf16x8_to_f16_perm(Aq[it]);
+    };
+
+    f32x16_t acc[M32][2];
+#pragma unroll
+    for (int mb = 0; mb < M32; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][cb][i] = 0.0f;
+
+    // dequantised operands of K step s (column blocks 0, 1)
+    auto dequant_k = [&](const Slot& sl, int st, half8_t (&bf)[2]) __attribute__((always_inline)) {
+        const int g = st >> 1;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            half2_t s2, c2;
+            scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
+            bf[cb] = dequant8(sl.B[cb][st & 1][g], s2, c2);
+        }
+    };
+    // one stream of 8*M32 (K step, row block) products; fragment reads run PF
+    // products ahead; only VALU work (the next step's dequantisation) may move
+    // across products
+    auto compute = [&](int c, const Slot& sl) __attribute__((always_inline)) {
+        const int buf = c & 1;
+        constexpr int NS = 8 * M32;
+        constexpr int PF = 4;
+        auto frag = [&](int p) __attribute__((always_inline)) {
+            return *reinterpret_cast<const half8_t*>(&As[buf][32 * (p % M32) + c32][16 * (p / M32) + 8 * kb]);
+        };
+        half8_t afr[NS];
+#pragma unroll
+        for (int q = 0; q < PF && q < NS; ++q) afr[q] = frag(q);
+        half8_t bfa[2], bfb[2];
+        dequant_k(sl, 0, bfa);
+#pragma unroll
+        for (int p = 0; p < NS; ++p) {
+            const int st = p / M32;
+            const int mb = p % M32;
+            if (p + PF < NS) afr[p + PF] = frag(p + PF);
+            if (mb == 0 && st < 7) dequant_k(sl, st + 1, (st & 1) ? bfa : bfb);
+            half8_t(&cur)[2] = (st & 1) ? bfb : bfa;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[p], cur[cb], acc[mb][cb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0x0002);
+        }
+    };
+
+    Slot s0, s1, s2;
+    load_A(0);
+    load_B(0, s0);
+    load_B(min(1, nch - 1), s1);
+    load_B(min(2, nch - 1), s2);
+    store_A(0);
+    lds_barrier();
+    auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
+        load_A(min(c + 1, nch - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(c, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        load_B(min(c + 3, nch - 1), cur);
+        __builtin_amdgcn_sched_barrier(0);
+        store_A((c + 1) & 1);
+        lds_barrier();
+    };
+    int c = 0;
+    for (; c + 3 <= nch; c += 3) {
+        step(c, s0);
+        step(c + 1, s1);
+        step(c + 2, s2);
+    }
+    if (c < nch) step(c, s0);
+    if (c + 1 < nch) step(c + 1, s1);
+
+    // epilogue: element i of lane l is tile row 32 mb + 8(i/4) + 4 kb + i%4, column c32
+#pragma unroll
+    for (int mb = 0; mb < M32; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
+            if (rl >= ti.rows) continue;
+            const size_t orow = (size_t)(ti.row0 + rl);
+            if (GATEUP) {
+                const uint32_t gb = f32_to_bf16_bits(acc[mb][0][i]);
+                const uint32_t ub = f32_to_bf16_bits(acc[mb][1][i]);
+                const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
+                const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
+                static_cast<uint16_t*>(a.out)[orow * N + n0 + c32] = (uint16_t)hb;
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    static_cast<uint16_t*>(a.out)[orow * N + n0 + 32 * cb + c32] =
+                        (uint16_t)f32_to_bf16_bits(acc[mb][cb][i]);
+            }
+        }
+    }
+}
+
 // Tiles of at most 16 rows (decode): the weights dominate the bytes, so each
 // wave streams its 64 weight rows (4 fragments per chunk) independently, with
 // no workgroup barrier and no LDS.  Bytes in flight set the speed here: the
@@ -745,6 +933,13 @@ void launch_tiles(GroupedArgs a, int S, hipStream_t st) {
                        a);
 }
 
+template <int OP, int M32>
+void launch_tiles32(GroupedArgs a, int S, hipStream_t st) {
+    a.n_chunks = OP == 0 ? a.N / 128 : a.N / 256;
+    const long tiles = ((long)S + (long)a.E * (32 * M32 - 1)) / (32 * M32) + 1;
+    hipLaunchKernelGGL((k_grouped32<OP, M32>), dim3(8 * moe::per_xcd(tiles * a.n_chunks)), dim3(256), 0, st, a);
+}
+
 template <int MODE, int OP>
 int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
     // exact mode keeps its accumulators in VGPRs (the group folds are VALU work)
@@ -766,8 +961,8 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
         case 2: launch_tiles<MODE, OP, 2, pick_cb(MODE, 2)>(a, S, st); break;
         case 4: launch_tiles<MODE, OP, 4, pick_cb(MODE, 4)>(a, S, st); break;
         case 6: launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st); break;
-        case 8: launch_tiles<MODE, OP, 8, pick_cb(MODE, 8)>(a, S, st); break;
-        default: launch_tiles<MODE, OP, 12, pick_cb(MODE, 12)>(a, S, st); break;
+        case 8: launch_tiles32<OP, 4>(a, S, st); break;
+        default: launch_tiles32<OP, 6>(a, S, st); break;
         }
     }
     return moe::launch_status(what);
