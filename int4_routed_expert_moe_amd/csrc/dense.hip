@@ -111,23 +111,26 @@ __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
     }
     const int active_mb = (rows + 15) >> 4;
 
-    // A staging: each thread moves A_ITERS 16-byte pieces of one row (rows past the
-    // tile read the tile's first row; their products are never stored)
+    // A staging: each load instruction of a wave reads 4 whole row chunks (16 lanes
+    // x 16 contiguous bytes); wave w moves rows 4*A_ITERS*w + 4*it + lane/16 (rows
+    // past the tile read the tile's first row; their products are never stored)
     constexpr int A_ITERS = BM * 16 / 256;
-    static_assert(BM * 16 % 256 == 0 && A_ITERS <= 16 && 16 % A_ITERS == 0, "A staging");
-    const int srow = (tid * A_ITERS) >> 4;
-    const int spiece = (tid * A_ITERS) & 15;
-    const uint16_t* aptr = a.x + (size_t)(m0 + (srow < rows ? srow : 0)) * K + spiece * 8;
+    static_assert(BM * 16 % 256 == 0 && A_ITERS * 16 == BM, "A staging");
+    auto srow_of = [&](int it) { return 4 * A_ITERS * wave + 4 * it + (lane >> 4); };
+    const uint16_t* aptr[A_ITERS];
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it)
+        aptr[it] = a.x + (size_t)(m0 + (srow_of(it) < rows ? srow_of(it) : 0)) * K + (lane & 15) * 8;
     u32x4_t Aq[A_ITERS];
     auto load_A = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it)
-            Aq[it] = *reinterpret_cast<const u32x4_t*>(aptr + (size_t)c * kDKC + 8 * it);
+            Aq[it] = *reinterpret_cast<const u32x4_t*>(aptr[it] + (size_t)c * kDKC);
     };
     auto store_A = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it)
-            *reinterpret_cast<u32x4_t*>(&As[buf][srow][(spiece + it) * 8]) = Aq[it];
+            *reinterpret_cast<u32x4_t*>(&As[buf][srow_of(it)][(lane & 15) * 8]) = Aq[it];
     };
 
     struct Slot {

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     // activation staging: a bf16 row chunk is 16 pieces of 16 B, an int8 row chunk 8
     constexpr int PIECES = EXACT ? 8 : 16;
     constexpr int A_ITERS = BM * PIECES / 256;
-    static_assert(BM * PIECES % 256 == 0 && A_ITERS <= PIECES, "staging pieces must tile the workgroup");
+    static_assert(BM * PIECES % 256 == 0 && A_ITERS * (64 / PIECES) * 4 == BM, "staging pieces must tile the workgroup");
 
     __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][kAStride];
     __shared__ __attribute__((aligned(16))) float SXs[2][4][EXACT ? BM : 1];
@@ -266,18 +266,19 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     }
     lds_barrier();  // rowsrc visible
 
-    // staging: this thread moves the A_ITERS consecutive 16-byte pieces starting at
-    // piece tid*A_ITERS of the tile chunk (within one row, or across the end of one
-    // row into the next); rows past the tile take the tile's first row
+    // staging: each load instruction of a wave reads RPI whole row chunks (PIECES
+    // lanes x 16 contiguous bytes per row), so every cache line it touches is used
+    // whole; wave w moves rows A_ITERS*RPI*w + RPI*it + lane/PIECES.  Rows past the
+    // tile take the tile's first row.
     constexpr int PIECE_ELEMS = EXACT ? 16 : 8;
-    const int lin0 = tid * A_ITERS;
-    const int srow = lin0 / PIECES;
-    const int spiece = lin0 % PIECES;
-    const int src0 = rowsrc[srow];
-    const int src1 = rowsrc[min(srow + 1, BM - 1)];
-    const int aoff0 = (src0 >= 0 ? src0 : rowsrc[0]) * K + spiece * PIECE_ELEMS;
-    const int aoff1 = (src1 >= 0 ? src1 : rowsrc[0]) * K - (PIECES - spiece) * PIECE_ELEMS;
-    auto piece_off = [&](int it) -> int { return (spiece + it < PIECES ? aoff0 : aoff1) + it * PIECE_ELEMS; };
+    constexpr int RPI = 64 / PIECES;
+    auto srow_of = [&](int it) { return A_ITERS * RPI * wave + RPI * it + lane / PIECES; };
+    int aoff[A_ITERS];
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) {
+        const int src = rowsrc[srow_of(it)];
+        aoff[it] = (src >= 0 ? src : rowsrc[0]) * K + (lane % PIECES) * PIECE_ELEMS;
+    }
     int sxrow = 0;
     if (EXACT && tid < BM) sxrow = rowsrc[tid] >= 0 ? rowsrc[tid] : rowsrc[0];
 
@@ -300,9 +301,9 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
             if (!EXACT)
-                Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + piece_off(it) + c * kKC);
+                Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + aoff[it] + c * kKC);
             else
-                Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + piece_off(it) + c * kKC);
+                Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + aoff[it] + c * kKC);
         }
         if (EXACT && tid < BM)
             SXq = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)sxrow * (K / 32) + c * 4);
@@ -310,9 +311,8 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     auto store_A = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
-            const bool same = spiece + it < PIECES;
-            const int row = same ? srow : srow + 1;
-            const int piece = same ? spiece + it : spiece + it - PIECES;
+            const int row = srow_of(it);
+            const int piece = lane % PIECES;
             if (!EXACT) {
                 *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = bf16x8_to_f16_perm(Aq[it]);
             } else {
