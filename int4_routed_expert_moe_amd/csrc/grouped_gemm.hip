@@ -611,8 +611,11 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
         }
     };
     // one stream of 8*M32 (K step, row block) products; fragment reads run PF
-    // products ahead; only VALU work (the next step's dequantisation) may move
-    // across products
+    // products ahead; only VALU work (the next step's dequantisation, the staged
+    // chunk's conversion) may move across products.  Halfway through, the next
+    // activation chunk (loaded since the step began) is converted and written
+    // to the other LDS buffer, whose last readers finished before the previous
+    // barrier.
     auto compute = [&](int c, const Slot& sl) __attribute__((always_inline)) {
         const int buf = c & 1;
         constexpr int NS = 8 * M32;
@@ -630,6 +633,7 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
             const int st = p / M32;
             const int mb = p % M32;
             if (p + PF < NS) afr[p + PF] = frag(p + PF);
+            if (p == NS / 2) store_A((c + 1) & 1);
             if (mb == 0 && st < 7) dequant_k(sl, st + 1, (st & 1) ? bfa : bfb);
             half8_t(&cur)[2] = (st & 1) ? bfb : bfa;
 #pragma unroll
@@ -652,8 +656,6 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
         compute(c, cur);
         __builtin_amdgcn_sched_barrier(0);
         load_B(min(c + 3, nch - 1), cur);
-        __builtin_amdgcn_sched_barrier(0);
-        store_A((c + 1) & 1);
         lds_barrier();
     };
     int c = 0;
