@@ -83,8 +83,8 @@ const char* moe_last_error_detail(void);
  * x [T,H] bf16; w_router [E,H] bf16; bias [E] fp32;
  * out: topk_idx [T,k] int32, topk_w [T,k] fp32.
  * ws: device workspace of at least moe_route_workspace_bytes(T, H, E) bytes,
- * 16-byte aligned (it holds the 64-wide block sums for up to 256 tokens, else
- * the fp32 logits).
+ * 16-byte aligned (it holds the fp32 logits and, for up to 256 tokens, the
+ * 64-wide block sums).
  * Results are bit-exact and deterministic. */
 size_t moe_route_workspace_bytes(int T, int H, int E);
 int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,

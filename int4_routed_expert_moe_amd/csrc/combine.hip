@@ -10,60 +10,75 @@
 
 namespace {
 
-// One workgroup per token; each thread owns 8 consecutive columns.  The k
-// slot rows are gathered through slot_pos; fp32 multiply then add, slots in
+// Grid (token, 2048-column block); each thread owns 8 consecutive columns.  The
+// KMAX slot rows are gathered through slot_pos with every load issued before
+// the sum; slots past k repeat the last slot with weight 0 (adding w*y = +-0 to
+// a sum that starts at +0 changes no bit).  fp32 multiply then add, slots in
 // ascending order.
-template <int MODE>
+template <int MODE, int KMAX>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, const int32_t* __restrict__ slot_pos,
                                                  const float* __restrict__ topk_w,
                                                  const uint16_t* __restrict__ shared, int k, int H,
                                                  void* __restrict__ out) {
     const int t = blockIdx.x;
-    for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
-        float acc[8];
+    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+    if (c >= H) return;
+    int pj[KMAX];
+    float wj[KMAX];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int jj = 0; jj < k; ++jj) {
-            const int p = slot_pos[(size_t)t * k + jj];
-            const float wj = topk_w[(size_t)t * k + jj];
-            if (MODE == MOE_MODE_BF16) {
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(y) + (size_t)p * H + c);
+    for (int jj = 0; jj < KMAX; ++jj) {
+        const int js = min(jj, k - 1);
+        pj[jj] = slot_pos[(size_t)t * k + js];
+        const float w = topk_w[(size_t)t * k + js];
+        wj[jj] = jj < k ? w : 0.0f;
+    }
+    float acc[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = acc[2 * q] + wj * __uint_as_float(v[q] << 16);
-                    acc[2 * q + 1] = acc[2 * q + 1] + wj * __uint_as_float(v[q] & 0xFFFF0000u);
-                }
-            } else {
-                const float* yr = static_cast<const float*>(y) + (size_t)p * H + c;
-                const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(yr);
-                const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(yr + 4);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    if (MODE == MOE_MODE_BF16) {
+        u32x4_t v[KMAX];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[q] = acc[q] + wj * v0[q];
-                    acc[4 + q] = acc[4 + q] + wj * v1[q];
-                }
-            }
-        }
-        if (MODE == MOE_MODE_BF16) {
-            u32x4_t o;
-            u32x4_t sh = {0u, 0u, 0u, 0u};
-            if (shared) sh = *reinterpret_cast<const u32x4_t*>(shared + (size_t)t * H + c);
+        for (int jj = 0; jj < KMAX; ++jj)
+            v[jj] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(y) + (size_t)pj[jj] * H + c);
+#pragma unroll
+        for (int jj = 0; jj < KMAX; ++jj)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                uint32_t lo = f32_to_bf16_bits(acc[2 * q]);
-                uint32_t hi = f32_to_bf16_bits(acc[2 * q + 1]);
-                if (shared) {
-                    lo = f32_to_bf16_bits(bf16_bits_to_f32(lo) + __uint_as_float(sh[q] << 16));
-                    hi = f32_to_bf16_bits(bf16_bits_to_f32(hi) + __uint_as_float(sh[q] & 0xFFFF0000u));
-                }
-                o[q] = lo | (hi << 16);
+                acc[2 * q] = acc[2 * q] + wj[jj] * __uint_as_float(v[jj][q] << 16);
+                acc[2 * q + 1] = acc[2 * q + 1] + wj[jj] * __uint_as_float(v[jj][q] & 0xFFFF0000u);
             }
-            *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(out) + (size_t)t * H + c) = o;
-        } else {
-            float* orow = static_cast<float*>(out) + (size_t)t * H + c;
-            *reinterpret_cast<f32x4_t*>(orow) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
-            *reinterpret_cast<f32x4_t*>(orow + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
+        u32x4_t o;
+        u32x4_t sh = {0u, 0u, 0u, 0u};
+        if (shared) sh = *reinterpret_cast<const u32x4_t*>(shared + (size_t)t * H + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t lo = f32_to_bf16_bits(acc[2 * q]);
+            uint32_t hi = f32_to_bf16_bits(acc[2 * q + 1]);
+            if (shared) {
+                lo = f32_to_bf16_bits(bf16_bits_to_f32(lo) + __uint_as_float(sh[q] << 16));
+                hi = f32_to_bf16_bits(bf16_bits_to_f32(hi) + __uint_as_float(sh[q] & 0xFFFF0000u));
+            }
+            o[q] = lo | (hi << 16);
         }
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(out) + (size_t)t * H + c) = o;
+    } else {
+        f32x4_t v0[KMAX], v1[KMAX];
+#pragma unroll
+        for (int jj = 0; jj < KMAX; ++jj) {
+            const float* yr = static_cast<const float*>(y) + (size_t)pj[jj] * H + c;
+            v0[jj] = *reinterpret_cast<const f32x4_t*>(yr);
+            v1[jj] = *reinterpret_cast<const f32x4_t*>(yr + 4);
+        }
+#pragma unroll
+        for (int jj = 0; jj < KMAX; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[q] = acc[q] + wj[jj] * v0[jj][q];
+                acc[4 + q] = acc[4 + q] + wj[jj] * v1[jj][q];
+            }
+        float* orow = static_cast<float*>(out) + (size_t)t * H + c;
+        *reinterpret_cast<f32x4_t*>(orow) = f32x4_t{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<f32x4_t*>(orow + 4) = f32x4_t{acc[4], acc[5], acc[6], acc[7]};
     }
 }
 
@@ -118,10 +133,14 @@ extern "C" int moe_combine(int mode, const void* y, const int32_t* slot_pos, con
     if (!aligned16(y) || !aligned16(out) || (shared && !aligned16(shared)))
         return fail(MOE_ERR_INVALID_ARG, "%s: y, out, shared must be 16-byte aligned", what);
     hipStream_t st = as_stream(stream);
-    if (mode == MOE_MODE_BF16)
-        hipLaunchKernelGGL(k_combine<MOE_MODE_BF16>, dim3(T), dim3(256), 0, st, y, slot_pos, topk_w, shared, k, H, out);
-    else
-        hipLaunchKernelGGL(k_combine<MOE_MODE_EXACT_I8>, dim3(T), dim3(256), 0, st, y, slot_pos, topk_w, nullptr, k, H, out);
+    const dim3 grid((unsigned)T, (unsigned)((H / 8 + 255) / 256));
+    if (mode == MOE_MODE_BF16) {
+        if (k <= 8) hipLaunchKernelGGL((k_combine<MOE_MODE_BF16, 8>), grid, dim3(256), 0, st, y, slot_pos, topk_w, shared, k, H, out);
+        else hipLaunchKernelGGL((k_combine<MOE_MODE_BF16, 16>), grid, dim3(256), 0, st, y, slot_pos, topk_w, shared, k, H, out);
+    } else {
+        if (k <= 8) hipLaunchKernelGGL((k_combine<MOE_MODE_EXACT_I8, 8>), grid, dim3(256), 0, st, y, slot_pos, topk_w, nullptr, k, H, out);
+        else hipLaunchKernelGGL((k_combine<MOE_MODE_EXACT_I8, 16>), grid, dim3(256), 0, st, y, slot_pos, topk_w, nullptr, k, H, out);
+    }
     return launch_status(what);
 }
 

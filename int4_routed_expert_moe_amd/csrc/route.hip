@@ -164,12 +164,33 @@ __global__ __launch_bounds__(256) void k_router_partials(const uint16_t* __restr
     }
 }
 
+// logits[t][e] = sum of the block sums P[t][b][e] in ascending b, one thread
+// per (token, expert); the loads of 16 blocks are issued before their adds.
+__global__ __launch_bounds__(256) void k_router_blocksum(const float* __restrict__ P, int T, int NB, int E,
+                                                         float* __restrict__ logits) {
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)T * E) return;
+    const long t = idx / E;
+    const int e = (int)(idx % E);
+    const float* src = P + (size_t)t * NB * E + e;
+    float total = 0.0f;
+    constexpr int BB = 16;
+    int b = 0;
+    for (; b + BB <= NB; b += BB) {
+        float v[BB];
+#pragma unroll
+        for (int u = 0; u < BB; ++u) v[u] = src[(size_t)(b + u) * E];
+#pragma unroll
+        for (int u = 0; u < BB; ++u) total = total + v[u];
+    }
+    for (; b < NB; ++b) total = total + src[(size_t)b * E];
+    logits[idx] = total;
+}
+
 // One wave per token: scores, biased ranking keys, k rounds of a wave-wide
 // arg-max (larger key, then lower expert index), renormalisation in rank order.
-// With nb > 0 the logits are summed here from block sums P[t][b][e] in
-// ascending block order; otherwise they are read from logits[t][e].
 template <int NQ>
-__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int nb,
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E,
                                                     int k, int renormalize,
                                                     int32_t* __restrict__ topk_idx,
@@ -180,31 +201,8 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     float s[NQ], key[NQ];
     uint32_t taken = 0;
     float lg[NQ];
-    if (nb > 0) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) lg[q] = 0.0f;
-        const float* Pt = logits + (size_t)t * nb * E;
-        constexpr int BB = 8;  // block sums loaded per batch (all loads issued before the adds)
-        int b = 0;
-        for (; b + BB <= nb; b += BB) {
-            float v[BB][NQ];
-#pragma unroll
-            for (int u = 0; u < BB; ++u)
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) v[u][q] = Pt[(size_t)(b + u) * E + min(lane + MOE_WAVE * q, E - 1)];
-#pragma unroll
-            for (int u = 0; u < BB; ++u)
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) lg[q] = lg[q] + v[u][q];
-        }
-        for (; b < nb; ++b) {
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) lg[q] = lg[q] + Pt[(size_t)b * E + min(lane + MOE_WAVE * q, E - 1)];
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) lg[q] = logits[(size_t)t * E + min(lane + MOE_WAVE * q, E - 1)];
-    }
+    for (int q = 0; q < NQ; ++q) lg[q] = logits[(size_t)t * E + min(lane + MOE_WAVE * q, E - 1)];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int e = lane + MOE_WAVE * q;
@@ -257,9 +255,9 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
 }
 
 template <int NQ>
-void launch_topk(const float* logits, int nb, const float* bias, int T, int E, int k, int renorm,
+void launch_topk(const float* logits, const float* bias, int T, int E, int k, int renorm,
                  int32_t* idx, float* w, hipStream_t st) {
-    hipLaunchKernelGGL(k_route_topk<NQ>, dim3((T + 3) / 4), dim3(256), 0, st, logits, nb, bias, T, E,
+    hipLaunchKernelGGL(k_route_topk<NQ>, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, T, E,
                        k, renorm, idx, w);
 }
 
@@ -269,10 +267,13 @@ constexpr int kPartialsMaxT = 256;
 
 }  // namespace
 
-// Few tokens: block sums [T, H/64, E] fp32.  Many tokens: logits [T, E] fp32.
+// Logits [T, E] fp32 (256-byte aligned), and for few tokens the block sums
+// [T, H/64, E] fp32 after them.
+static size_t logits_bytes(int T, int E) { return (((size_t)T * (size_t)E * sizeof(float)) + 255) & ~(size_t)255; }
+
 extern "C" size_t moe_route_workspace_bytes(int T, int H, int E) {
     if (T <= 0 || E <= 0 || H <= 0) return 0;
-    if (T <= kPartialsMaxT) return (size_t)T * (size_t)(H / kRouteKC) * (size_t)E * sizeof(float);
+    if (T <= kPartialsMaxT) return logits_bytes(T, E) + (size_t)T * (size_t)(H / kRouteKC) * (size_t)E * sizeof(float);
     return (size_t)T * (size_t)E * sizeof(float);
 }
 
@@ -298,21 +299,24 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const floa
     hipStream_t st = as_stream(stream);
     float* logits = static_cast<float*>(ws);
     const int tb = (T + kRouteTok - 1) / kRouteTok;
-    int nb = 0;
     if (T <= kPartialsMaxT) {
-        nb = H / kRouteKC;
-        dim3 grid(nb, (E + 63) / 64, tb);
-        hipLaunchKernelGGL(k_router_partials, grid, dim3(256), 0, st, x, w_router, T, H, E, logits);
+        const int NB = H / kRouteKC;
+        float* P = reinterpret_cast<float*>(static_cast<char*>(ws) + logits_bytes(T, E));
+        dim3 grid(NB, (E + 63) / 64, tb);
+        hipLaunchKernelGGL(k_router_partials, grid, dim3(256), 0, st, x, w_router, T, H, E, P);
+        if (int rc = launch_status("moe_route block sums")) return rc;
+        const long n = (long)T * E;
+        hipLaunchKernelGGL(k_router_blocksum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, T, NB, E, logits);
     } else {
         hipLaunchKernelGGL(k_router_full, dim3((E + 63) / 64, tb), dim3(256), 0, st, x, w_router, T, H, E, logits);
     }
     int rc = launch_status("moe_route logits");
     if (rc) return rc;
     const int nq = (E + MOE_WAVE - 1) / MOE_WAVE;
-    if (nq <= 1) launch_topk<1>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 2) launch_topk<2>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 4) launch_topk<4>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 8) launch_topk<8>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else launch_topk<16>(logits, nb, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    if (nq <= 1) launch_topk<1>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    else if (nq <= 2) launch_topk<2>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    else if (nq <= 4) launch_topk<4>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    else if (nq <= 8) launch_topk<8>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    else launch_topk<16>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
     return launch_status("moe_route topk");
 }

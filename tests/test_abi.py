@@ -68,7 +68,7 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert _status(lib, "moe_route", odd, fake, fake, 4, 256, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -1
     assert _status(lib, "moe_route", fake, fake, fake, 4, 256, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(8), null) == -3
     assert b"workspace" in lib.moe_last_error_detail()
-    assert lib.moe_route_workspace_bytes(64, 7168, 384) == 64 * (7168 // 64) * 384 * 4  # block sums
+    assert lib.moe_route_workspace_bytes(64, 7168, 384) == 64 * 384 * 4 + 64 * (7168 // 64) * 384 * 4  # logits + block sums
     assert lib.moe_route_workspace_bytes(4096, 7168, 384) == 4096 * 384 * 4  # logits
     # zero tokens is a no-op
     assert _status(lib, "moe_route", null, null, null, 0, 256, 16, 2, 1, null, null, null, ctypes.c_size_t(0), null) == 0
