@@ -43,6 +43,8 @@ class MoELayer:
     `experts` holds the routed weights in the checkpoint layout; they are
     permuted once into the fragment layout here."""
 
+    SIDE_STREAM_MIN_T = 1024  # tokens from which the shared expert runs on its own stream
+
     def __init__(self, cfg: dict, router_w, router_b, experts: dict, shared: dict | None = None,
                  latent: dict | None = None):
         self.cfg = dict(cfg)
@@ -55,6 +57,7 @@ class MoELayer:
         self.E, self.k, self.H, self.I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
         self.Kin = cfg.get("L") or cfg["H"]  # width the routed experts see
         self._ws = {}
+        self._side = None
         self.device = router_w.device
         if self.mode == _m.MOE_MODE_EXACT_I8 and (shared is not None or latent is not None):
             raise ValueError("exact mode is defined for the routed experts alone")
@@ -108,8 +111,8 @@ class MoELayer:
             Is = self.shared["wg"].shape[0]
             w["shared_h"] = torch.empty((T, Is), dtype=torch.bfloat16, device=dev)
             w["shared_out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-            dense_bytes = max(dense_bytes, _m.moe_dense_workspace_bytes(T, 2 * Is, H),
-                              _m.moe_dense_workspace_bytes(T, H, Is))
+            shared_bytes = max(_m.moe_dense_workspace_bytes(T, 2 * Is, H), _m.moe_dense_workspace_bytes(T, H, Is))
+            w["shared_ws"] = torch.empty(max(1, shared_bytes), dtype=torch.uint8, device=dev)
         if self.latent is not None:
             L = Kin
             w["x_lat"] = torch.empty((T, L), dtype=torch.bfloat16, device=dev)
@@ -124,12 +127,32 @@ class MoELayer:
     def forward(self, x: torch.Tensor, marks: list | None = None) -> torch.Tensor:
         """x [T, H] bf16 -> out [T, H] (bf16, or fp32 in exact mode).  Returns the
         workspace's output buffer; the intermediates stay in ``workspace(T)``.
-        ``marks``: when a list is given, a timing event on the current stream is
-        appended after every call as (call name, event)."""
+
+        The shared expert depends only on x, so for batches of at least
+        ``SIDE_STREAM_MIN_T`` tokens it runs on a second stream, overlapping the
+        router, the permutation and the routed GEMMs; the combine (or the latent
+        up-projection) waits for it.  (At decode sizes it would take CUs from the
+        HBM-bound routed GEMMs instead, measured slower.)  The side stream first
+        waits for an event recorded on the current stream, which orders it after
+        x and after the previous forward's use of its buffers.
+        ``marks``: when a list is given, every call runs on the current stream and
+        a timing event is appended after each as (call name, event)."""
         T = x.shape[0]
         w = self.workspace(T)
         if T == 0:
             return w["out"]
+        side = None
+        if self.shared is not None and marks is None and T >= self.SIDE_STREAM_MIN_T:
+            if self._side is None:
+                self._side = torch.cuda.Stream(device=self.device)
+                self._ev_fork = torch.cuda.Event()
+                self._ev_join = torch.cuda.Event()
+            side = self._side
+            self._ev_fork.record()
+            side.wait_event(self._ev_fork)
+            with torch.cuda.stream(side):
+                self._shared_expert(x, w)
+                self._ev_join.record()
 
         def mark(name):
             if marks is not None:
@@ -151,10 +174,8 @@ class MoELayer:
             act = w["x_lat"]
         shared_out = None
         if self.shared is not None:
-            _m.moe_dense_swiglu_bf16(x, self.shared["wg"], self.shared["wu"], w["shared_h"], w["dense_ws"])
-            mark("shared_gate_up")
-            _m.moe_linear_bf16(w["shared_h"], self.shared["wd"], None, w["shared_out"], w["dense_ws"])
-            mark("shared_down")
+            if side is None:
+                self._shared_expert(x, w, mark)
             shared_out = w["shared_out"]
         if self.mode == _m.MOE_MODE_EXACT_I8:
             _m.moe_quant_act_int8(act, w["qx"], w["sx"])
@@ -168,6 +189,8 @@ class MoELayer:
         _m.moe_int4_grouped_down(self.mode, w["h"], w["h_scale"], ex["wd"], ex["sd"], w["offsets"], T, k, E, I,
                                  Kin, w["y"])
         mark("moe_int4_grouped_down")
+        if side is not None:
+            torch.cuda.current_stream().wait_event(self._ev_join)
         if self.latent is None:
             _m.moe_combine(self.mode, w["y"], w["slot_pos"], w["topk_w"], shared_out, T, k, H, w["out"])
             mark("moe_combine")
@@ -179,5 +202,13 @@ class MoELayer:
             _m.moe_linear_bf16(w["normed"], self.latent["w_up"], shared_out, w["out"], w["dense_ws"])
             mark("latent_up")
         return w["out"]
+
+    def _shared_expert(self, x, w, mark=None):
+        _m.moe_dense_swiglu_bf16(x, self.shared["wg"], self.shared["wu"], w["shared_h"], w["shared_ws"])
+        if mark:
+            mark("shared_gate_up")
+        _m.moe_linear_bf16(w["shared_h"], self.shared["wd"], None, w["shared_out"], w["shared_ws"])
+        if mark:
+            mark("shared_down")
 
     __call__ = forward
