@@ -108,9 +108,11 @@ def _counter_means(folder, counter):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            m = re.search(r"k_grouped(?:_skinny)?<(\d+), (\d+)", name)
-            if m:
-                key = "moe_int4_grouped_swiglu" if m.group(2) == "0" else "moe_int4_grouped_down"
+            m = re.search(r"k_grouped(?:_skinny)?<(\d+), (\d+)", name)   # <mode, op, ...>
+            m32 = re.search(r"k_grouped32<(\d+),", name)                   # <op, m32>
+            if m or m32:
+                op = m.group(2) if m else m32.group(1)
+                key = "moe_int4_grouped_swiglu" if op == "0" else "moe_int4_grouped_down"
             elif "opy" in name:
                 key = ("copy", int(r["Grid_Size"]))
             else:
