@@ -62,6 +62,7 @@ struct GroupedArgs {
     int n_chunks;   // column chunks per tile
     void* out;
     float* out_scale;
+    uint32_t act_bytes;  // size of act in bytes, when under 4 GiB (32x32 kernel's loads)
 };
 
 struct TileInfo {
@@ -131,6 +132,23 @@ __device__ bool locate_item(const int32_t* __restrict__ offsets, int E, int bm, 
     ti.row0 = __shfl(frow0, src);
     ti.rows = __shfl(frows, src);
     return true;
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled whatever the body's size.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Descriptor for raw buffer loads from `bytes` bytes at p (gfx9 family: the
+// fourth word selects the 32-bit data format).  Offsets are 32-bit, and loads
+// past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
 // First fragment (chunk 0) of 16-row group n16 of expert e in a prepacked
@@ -519,6 +537,7 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
     constexpr int A_ITERS = BM * PIECES / 256;
     constexpr int AST = 144;  // halves per LDS row (128 + 16 pad)
     static_assert(BM % 16 == 0 && A_ITERS * 4 * 4 == BM, "staging: 4 rows per wave instruction");
+    static_assert(8 * M32 == 4 * A_ITERS, "staging: one activation piece every 4 products");
 
     __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][AST];
     __shared__ int32_t rowsrc[BM];
@@ -559,12 +578,14 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
     // staging: each load instruction of a wave reads 4 whole row chunks (16 lanes x
     // 16 contiguous bytes per row), so every cache line it touches is used whole;
     // wave w moves rows A_ITERS*4*w + 4*it + lane/16.  Rows past the tile take the
-    // tile's first row.
-    int aoff[A_ITERS];
+    // tile's first row.  The loads are raw buffer loads with 32-bit byte offsets
+    // (the host launches this kernel only for activations under 4 GiB): one
+    // offset register per load, the chunk offset in a scalar register.
+    uint32_t aoff[A_ITERS];
 #pragma unroll
     for (int it = 0; it < A_ITERS; ++it) {
         const int src = rowsrc[A_ITERS * 4 * wave + 4 * it + (lane >> 4)];
-        aoff[it] = (src >= 0 ? src : rowsrc[0]) * K + (lane & 15) * 8;
+        aoff[it] = ((uint32_t)(src >= 0 ? src : rowsrc[0]) * (uint32_t)K + (uint32_t)(lane & 15) * 8u) * 2u;
     }
 
     struct Slot {
@@ -580,16 +601,21 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
         }
     };
     u32x4_t Aq[A_ITERS];
+    const __amdgpu_buffer_rsrc_t act_rsrc = buffer_rsrc(a.act, a.act_bytes);
+    auto load_piece = [&](int it, int c) __attribute__((always_inline)) {
+        Aq[it] = __builtin_amdgcn_raw_buffer_load_b128(act_rsrc, aoff[it], c * (kKC * 2), 0);
+    };
+    auto store_piece = [&](int it, int buf) __attribute__((always_inline)) {
+        *reinterpret_cast<u32x4_t*>(&As[buf][A_ITERS * 4 * wave + 4 * it + (lane >> 4)][(lane & 15) * 8]) =
+            bf16x8_to_f16_perm(Aq[it]);
+    };
     auto load_A = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < A_ITERS; ++it)
-            Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + aoff[it] + c * kKC);
+        for (int it = 0; it < A_ITERS; ++it) load_piece(it, c);
     };
     auto store_A = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < A_ITERS; ++it)
-            *reinterpret_cast<u32x4_t*>(&As[buf][A_ITERS * 4 * wave + 4 * it + (lane >> 4)][(lane & 15) * 8]) =
-                bf16x8_to_f16_perm(Aq[it]);
+        for (int it = 0; it < A_ITERS; ++it) store_piece(it, buf);
     };
 
     f32x16_t acc[M32][2];
@@ -612,10 +638,15 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
     };
     // one stream of 8*M32 (K step, row block) products; fragment reads run PF
     // products ahead; only VALU work (the next step's dequantisation, the staged
-    // chunk's conversion) may move across products.  Halfway through, the next
-    // activation chunk (loaded since the step began) is converted and written
-    // to the other LDS buffer, whose last readers finished before the previous
-    // barrier.
+    // chunk's conversion) may move across products.  The next activation chunk
+    // is staged one piece every 4 products (8*M32 = 4*A_ITERS): piece i, loaded
+    // at the same point of the previous chunk, is converted and written to the
+    // other LDS buffer (whose last readers finished before the previous
+    // barrier), and the same piece of the chunk after is loaded into the freed
+    // registers.  Loads retire in issue order, so each piece's wait leaves the
+    // 17 younger loads (11 pieces, 6 weight pieces) in flight: it covers only
+    // loads issued a whole chunk earlier, and the conversion work is spread
+    // among the products instead of stalling them at one point.
     auto compute = [&](int c, const Slot& sl) __attribute__((always_inline)) {
         const int buf = c & 1;
         constexpr int NS = 8 * M32;
@@ -628,31 +659,37 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
         for (int q = 0; q < PF && q < NS; ++q) afr[q] = frag(q);
         half8_t bfa[2], bfb[2];
         dequant_k(sl, 0, bfa);
-#pragma unroll
-        for (int p = 0; p < NS; ++p) {
-            const int st = p / M32;
-            const int mb = p % M32;
-            if (p + PF < NS) afr[p + PF] = frag(p + PF);
-            if (p == NS / 2) store_A((c + 1) & 1);
-            if (mb == 0 && st < 7) dequant_k(sl, st + 1, (st & 1) ? bfa : bfb);
+        static_for<NS>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int p = decltype(pc)::value;
+            constexpr int st = p / M32;
+            constexpr int mb = p % M32;
+            if constexpr (p + PF < NS) afr[p + PF] = frag(p + PF);
+            if constexpr (p % 4 == 2) {
+                store_piece(p / 4, (c + 1) & 1);
+                load_piece(p / 4, min(c + 2, nch - 1));
+            }
+            if constexpr (mb == 0 && st < 7) dequant_k(sl, st + 1, (st & 1) ? bfa : bfb);
             half8_t(&cur)[2] = (st & 1) ? bfb : bfa;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
                 acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[p], cur[cb], acc[mb][cb], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0x0002);
-        }
+        });
     };
 
+    // prologue: the loads in flight at each step's start are, in issue order,
+    // weights c, weights c+1, activations c+1, weights c+2 (so the midpoint
+    // wait for activations c+1 leaves weights c+2 in flight), in the first
+    // step as in every later one
     Slot s0, s1, s2;
     load_A(0);
     load_B(0, s0);
     load_B(min(1, nch - 1), s1);
-    load_B(min(2, nch - 1), s2);
     store_A(0);
+    load_A(min(1, nch - 1));
+    load_B(min(2, nch - 1), s2);
     lds_barrier();
     auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
-        load_A(min(c + 1, nch - 1));
-        __builtin_amdgcn_sched_barrier(0);
         compute(c, cur);
         __builtin_amdgcn_sched_barrier(0);
         load_B(min(c + 3, nch - 1), cur);
@@ -963,8 +1000,16 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
         case 2: launch_tiles<MODE, OP, 2, pick_cb(MODE, 2)>(a, S, st); break;
         case 4: launch_tiles<MODE, OP, 4, pick_cb(MODE, 4)>(a, S, st); break;
         case 6: launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st); break;
-        case 8: launch_tiles32<OP, 4>(a, S, st); break;
-        default: launch_tiles32<OP, 6>(a, S, st); break;
+        default: {
+            // the 32x32 kernel addresses activation rows with 32-bit byte offsets
+            const size_t act_rows = OP == 0 ? (size_t)S / (size_t)a.k : (size_t)S;
+            const size_t act_bytes = act_rows * (size_t)a.K * 2;
+            a.act_bytes = (uint32_t)act_bytes;
+            if (act_bytes >= ((size_t)1 << 32)) launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st);
+            else if (mb == 8) launch_tiles32<OP, 4>(a, S, st);
+            else launch_tiles32<OP, 6>(a, S, st);
+            break;
+        }
         }
     }
     return moe::launch_status(what);
