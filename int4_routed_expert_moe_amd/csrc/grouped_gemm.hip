@@ -537,7 +537,6 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
     constexpr int A_ITERS = BM * PIECES / 256;
     constexpr int AST = 144;  // halves per LDS row (128 + 16 pad)
     static_assert(BM % 16 == 0 && A_ITERS * 4 * 4 == BM, "staging: 4 rows per wave instruction");
-    static_assert(8 * M32 == 4 * A_ITERS, "staging: one activation piece every 4 products");
 
     __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][AST];
     __shared__ int32_t rowsrc[BM];
@@ -636,38 +635,44 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
             bf[cb] = dequant8(sl.B[cb][st & 1][g], s2, c2);
         }
     };
-    // one stream of 8*M32 (K step, row block) products; fragment reads run PF
-    // products ahead; only VALU work (the next step's dequantisation, the staged
-    // chunk's conversion) may move across products.  The next activation chunk
-    // is staged one piece every 4 products (8*M32 = 4*A_ITERS): piece i, loaded
-    // at the same point of the previous chunk, is converted and written to the
-    // other LDS buffer (whose last readers finished before the previous
-    // barrier), and the same piece of the chunk after is loaded into the freed
-    // registers.  Loads retire in issue order, so each piece's wait leaves the
-    // 17 younger loads (11 pieces, 6 weight pieces) in flight: it covers only
-    // loads issued a whole chunk earlier, and the conversion work is spread
-    // among the products instead of stalling them at one point.
-    auto compute = [&](int c, const Slot& sl) __attribute__((always_inline)) {
-        const int buf = c & 1;
-        constexpr int NS = 8 * M32;
+    // One stream of 8*NACT (K step, row block) products over the tile's NACT
+    // active row blocks (blocks wholly past its rows are skipped); fragment
+    // reads run PF products ahead; only VALU work (the next step's
+    // dequantisation, the staged chunk's conversion) may move across products.
+    // The next activation chunk is staged piece by piece, the A_ITERS pieces
+    // spread evenly over the products: piece i, loaded at the same point of the
+    // previous chunk, is converted and written to the other LDS buffer (whose
+    // last readers finished before the previous barrier), and the same piece of
+    // the chunk after is loaded into the freed registers.  Loads retire in issue
+    // order, so each piece's wait leaves the younger pieces and the newest
+    // weight slot in flight: it covers only loads issued a whole chunk earlier,
+    // and the conversion work is spread among the products instead of stalling
+    // them at one point.
+    auto compute = [&](auto nact, int c, const Slot& sl) __attribute__((always_inline)) {
+        constexpr int NACT = decltype(nact)::value;
+        constexpr int NS = 8 * NACT;
         constexpr int PF = 4;
+        const int buf = c & 1;
         auto frag = [&](int p) __attribute__((always_inline)) {
-            return *reinterpret_cast<const half8_t*>(&As[buf][32 * (p % M32) + c32][16 * (p / M32) + 8 * kb]);
+            return *reinterpret_cast<const half8_t*>(&As[buf][32 * (p % NACT) + c32][16 * (p / NACT) + 8 * kb]);
         };
         half8_t afr[NS];
 #pragma unroll
-        for (int q = 0; q < PF && q < NS; ++q) afr[q] = frag(q);
+        for (int q = 0; q < PF; ++q) afr[q] = frag(q);
         half8_t bfa[2], bfb[2];
         dequant_k(sl, 0, bfa);
         static_for<NS>([&](auto pc) __attribute__((always_inline)) {
             constexpr int p = decltype(pc)::value;
-            constexpr int st = p / M32;
-            constexpr int mb = p % M32;
+            constexpr int st = p / NACT;
+            constexpr int mb = p % NACT;
             if constexpr (p + PF < NS) afr[p + PF] = frag(p + PF);
-            if constexpr (p % 4 == 2) {
-                store_piece(p / 4, (c + 1) & 1);
-                load_piece(p / 4, min(c + 2, nch - 1));
-            }
+            static_for<A_ITERS>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr ((2 * i + 1) * NS / (2 * A_ITERS) == p) {  // piece i at the middle of its share
+                    store_piece(i, (c + 1) & 1);
+                    load_piece(i, min(c + 2, nch - 1));
+                }
+            });
             if constexpr (mb == 0 && st < 7) dequant_k(sl, st + 1, (st & 1) ? bfa : bfb);
             half8_t(&cur)[2] = (st & 1) ? bfb : bfa;
 #pragma unroll
@@ -678,31 +683,38 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
     };
 
     // prologue: the loads in flight at each step's start are, in issue order,
-    // weights c, weights c+1, activations c+1, weights c+2 (so the midpoint
-    // wait for activations c+1 leaves weights c+2 in flight), in the first
-    // step as in every later one
-    Slot s0, s1, s2;
-    load_A(0);
-    load_B(0, s0);
-    load_B(min(1, nch - 1), s1);
-    store_A(0);
-    load_A(min(1, nch - 1));
-    load_B(min(2, nch - 1), s2);
-    lds_barrier();
-    auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
-        compute(c, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        load_B(min(c + 3, nch - 1), cur);
+    // weights c, weights c+1, activations c+1, weights c+2 (so a piece's wait
+    // leaves weights c+2 in flight), in the first step as in every later one
+    auto main_loop = [&](auto nact) __attribute__((always_inline)) {
+        Slot s0, s1, s2;
+        load_A(0);
+        load_B(0, s0);
+        load_B(min(1, nch - 1), s1);
+        store_A(0);
+        load_A(min(1, nch - 1));
+        load_B(min(2, nch - 1), s2);
         lds_barrier();
+        auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
+            compute(nact, c, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            load_B(min(c + 3, nch - 1), cur);
+            lds_barrier();
+        };
+        int c = 0;
+        for (; c + 3 <= nch; c += 3) {
+            step(c, s0);
+            step(c + 1, s1);
+            step(c + 2, s2);
+        }
+        if (c < nch) step(c, s0);
+        if (c + 1 < nch) step(c + 1, s1);
     };
-    int c = 0;
-    for (; c + 3 <= nch; c += 3) {
-        step(c, s0);
-        step(c + 1, s1);
-        step(c + 2, s2);
-    }
-    if (c < nch) step(c, s0);
-    if (c + 1 < nch) step(c + 1, s1);
+    // one branch-free instance of the loop per active row-block count
+    const int nact = (ti.rows + 31) >> 5;
+    static_for<M32>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int n = decltype(ic)::value + 1;
+        if (nact == n) main_loop(std::integral_constant<int, n>{});
+    });
 
     // epilogue: element i of lane l is tile row 32 mb + 8(i/4) + 4 kb + i%4, column c32
 #pragma unroll
