@@ -108,7 +108,7 @@ def _counter_means(folder, counter):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            m = re.search(r"k_grouped(?:_skinny)?<(\d+), (\d+)", name)   # <mode, op, ...>
+            m = re.search(r"k_grouped(?:_skinny|_exact)?<(\d+), (\d+)", name)   # <mode, op, ...>
             m32 = re.search(r"k_grouped32<(\d+),", name)                   # <op, m32>
             if m or m32:
                 op = m.group(2) if m else m32.group(1)

@@ -128,9 +128,12 @@ __device__ bool locate_item(const int32_t* __restrict__ offsets, int E, int bm, 
             }
         }
     }
-    ti.e = __shfl(fe, src);
-    ti.row0 = __shfl(frow0, src);
-    ti.rows = __shfl(frows, src);
+    // wave-uniform by construction; reading them through readfirstlane puts them
+    // (and the fragment bases derived from them) in scalar registers
+    ti.e = __builtin_amdgcn_readfirstlane(__shfl(fe, src));
+    ti.row0 = __builtin_amdgcn_readfirstlane(__shfl(frow0, src));
+    ti.rows = __builtin_amdgcn_readfirstlane(__shfl(frows, src));
+    nc = __builtin_amdgcn_readfirstlane(nc);
     return true;
 }
 
@@ -149,6 +152,15 @@ __device__ __forceinline__ void static_for(F&& f) {
 // past the end return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// The same for an address and size that are wave-uniform but computed from
+// values the compiler cannot prove uniform: both are read from the first lane
+// (a descriptor it took for divergent would be used through a loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_uniform(const void* p, uint32_t bytes) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return buffer_rsrc(reinterpret_cast<const void*>(lo | (hi << 32)), (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
 }
 
 // First fragment (chunk 0) of 16-row group n16 of expert e in a prepacked
@@ -234,7 +246,7 @@ __device__ __forceinline__ void lds_barrier() {
 // past the tile's count read a valid row and are never written out (an
 // output row depends only on its own activation row).
 template <int MODE, int OP, int MB, int CB>
-__global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
+__device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
     static_assert(CB == 2 || CB == 4, "column blocks per wave");
     static_assert(CB == 4 || MODE == MOE_MODE_BF16, "exact mode quantises 32 output columns per wave");
     constexpr int BM = 16 * MB;
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15;   // row/column within a 16-block
     const int j = lane >> 4;   // k-block of the lane (0..3)
     const int K = a.K;
@@ -271,17 +283,25 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     // this wave's weight fragments, per column block (16 rows each): gate/up
     // waves own 8*CB output columns (CB/2 gate blocks, then the matching up
     // blocks), down waves 16*CB
-    const uint8_t* wf[CB];
-    const uint16_t* sf[CB];
+    // Weights and scales are read through buffer descriptors over the tile
+    // expert's fragments (the host bounds an expert's matrix below 2 GiB), with
+    // each column block's fragment offset in a scalar register and one lane
+    // offset shared by all blocks.
     const int n0 = GATEUP ? (nc * 4 + wave) * (8 * CB) : (nc * 4 + wave) * (16 * CB);
+    const uint32_t w_bytes = (uint32_t)(N / 16) * (uint32_t)nch * kFragBytes;
+    const uint32_t s_bytes = (uint32_t)(N / 16) * (uint32_t)nch * kFragScales * 2;
+    const __amdgpu_buffer_rsrc_t rw0 = buffer_rsrc_uniform(a.w0 + (size_t)ti.e * w_bytes, w_bytes);
+    const __amdgpu_buffer_rsrc_t rs0 = buffer_rsrc_uniform(a.s0 + (size_t)ti.e * (s_bytes / 2), s_bytes);
+    const __amdgpu_buffer_rsrc_t rw1 = GATEUP ? buffer_rsrc_uniform(a.w1 + (size_t)ti.e * w_bytes, w_bytes) : rw0;
+    const __amdgpu_buffer_rsrc_t rs1 = GATEUP ? buffer_rsrc_uniform(a.s1 + (size_t)ti.e * (s_bytes / 2), s_bytes) : rs0;
+    int woff[CB], soff[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const int n16 = (n0 >> 4) + (GATEUP ? (cb % (CB / 2)) : cb);
-        const bool second = GATEUP && cb >= CB / 2;
-        const size_t f = frag_index(ti.e, n16, N, nch);
-        wf[cb] = (second ? a.w1 : a.w0) + f * kFragBytes + lane * 16;
-        sf[cb] = (second ? a.s1 : a.s0) + f * kFragScales + 4 * r;
+        woff[cb] = __builtin_amdgcn_readfirstlane(n16 * nch * kFragBytes);
+        soff[cb] = __builtin_amdgcn_readfirstlane(n16 * nch * (kFragScales * 2));
     }
+    const uint32_t lane_w = (uint32_t)lane * 16u, lane_s = (uint32_t)r * 8u;
     lds_barrier();  // rowsrc visible
 
     // staging: each load instruction of a wave reads RPI whole row chunks (PIECES
@@ -309,8 +329,9 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
     auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            sl.B[cb] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
-            sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
+            const bool second = GATEUP && cb >= CB / 2;
+            sl.B[cb] = __builtin_amdgcn_raw_buffer_load_b128(second ? rw1 : rw0, lane_w, woff[cb] + c * kFragBytes, 0);
+            sl.S[cb] = __builtin_amdgcn_raw_buffer_load_b64(second ? rs1 : rs0, lane_s, soff[cb] + c * (kFragScales * 2), 0);
         }
     };
     u32x4_t Aq[A_ITERS];
@@ -358,41 +379,21 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
             bf[cb] = dequant8(sl.B[cb][g], s2, c2);
         }
     };
-    // NACT > 0 (bf16, tiles of 8 or more row blocks, sized so they run nearly
-    // full): all NACT row blocks with no branches, and the next step's
-    // dequantisation issued among the current step's matrix-core operations.
-    // NACT == 0: all MB row blocks, each under a uniform branch (keeps the
-    // register count of the smaller tiles, and of exact mode, in bounds).
+    // NACT > 0 (exact mode): one stream of 4*NACT (group step, row block)
+    // products over the tile's NACT active row blocks (blocks wholly past its
+    // rows are skipped; one branch-free instance per count).  Fragment and s_x
+    // reads run PF products ahead.  A product's results are folded one product
+    // later, so each fold reads matrix-core results issued four operations
+    // earlier instead of waiting on the newest one; per row, groups still fold
+    // in ascending order.  NACT == 0 (bf16): the row blocks under uniform
+    // branches.
     auto compute = [&](auto nact, int c, const Slot& sl) __attribute__((always_inline)) {
         constexpr int NACT = decltype(nact)::value;
-        const int buf = c & 1;
-        if constexpr (NACT > 0) {
-            // one stream of 4*NACT (group step, row block) products; fragment reads
-            // run PF products ahead, and only VALU work (the next group step's
-            // dequantisation) may move across products
-            constexpr int NS = 4 * NACT;
-            constexpr int PF = 4;
-            auto frag = [&](int st) __attribute__((always_inline)) {
-                return *reinterpret_cast<const half8_t*>(&As[buf][16 * (st % NACT) + r][32 * (st / NACT) + 8 * j]);
-            };
-            half8_t afr[NS];
-#pragma unroll
-            for (int q = 0; q < PF && q < NS; ++q) afr[q] = frag(q);
-            half8_t bfa[CB], bfb[CB];
-            dequant_step(sl, 0, bfa);
-#pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const int g = st / NACT;
-                const int mb = st % NACT;
-                if (st + PF < NS) afr[st + PF] = frag(st + PF);
-                if (mb == 0 && g < 3) dequant_step(sl, g + 1, (g & 1) ? bfa : bfb);
-                half8_t(&cur)[CB] = (g & 1) ? bfb : bfa;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-                    acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[st], cur[cb], acc[mb][cb], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0x0002);
-            }
-        } else {
+        if constexpr (NACT == 0) {
+            // bf16: all MB row blocks, each under a uniform branch on the tile's
+            // active count (fewer registers than the instances: this kernel
+            // serves HBM-bound batches, where two waves per SIMD matter more)
+            const int buf = c & 1;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 half8_t bf[CB];
@@ -401,62 +402,111 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
                 for (int mb = 0; mb < MB; ++mb) {
                     if (mb < active_mb) {
                         const half8_t af = *reinterpret_cast<const half8_t*>(&As[buf][16 * mb + r][32 * g + 8 * j]);
-                        if (!EXACT) {
 #pragma unroll
-                            for (int cb = 0; cb < CB; ++cb)
-                                acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
-                        } else {
-                            const f32x4_t sx = *reinterpret_cast<const f32x4_t*>(&SXs[buf][g][16 * mb + 4 * j]);
-#pragma unroll
-                            for (int cb = 0; cb < CB; ++cb) {
-                                const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                    af, bf[cb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) acc[mb][cb][i] = __builtin_fmaf(d[i], sx[i], acc[mb][cb][i]);
-                            }
-                        }
+                        for (int cb = 0; cb < CB; ++cb)
+                            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
                     }
                 }
             }
+        } else {
+        constexpr int NS = 4 * NACT;
+        constexpr int PF = EXACT ? 2 : 4;
+        const int buf = c & 1;
+        auto frag = [&](int st) __attribute__((always_inline)) {
+            return *reinterpret_cast<const half8_t*>(&As[buf][16 * (st % NACT) + r][32 * (st / NACT) + 8 * j]);
+        };
+        auto sxv = [&](int st) __attribute__((always_inline)) {
+            return *reinterpret_cast<const f32x4_t*>(&SXs[buf][st / NACT][16 * (st % NACT) + 4 * j]);
+        };
+        half8_t afr[NS];
+        f32x4_t sxr[NS];
+#pragma unroll
+        for (int q = 0; q < PF && q < NS; ++q) {
+            afr[q] = frag(q);
+            if constexpr (EXACT) sxr[q] = sxv(q);
+        }
+        half8_t bfa[CB], bfb[CB];
+        dequant_step(sl, 0, bfa);
+        f32x4_t d[2][CB];
+        auto fold = [&](auto sc) __attribute__((always_inline)) {
+            constexpr int st = decltype(sc)::value;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[st % NACT][cb][i] = __builtin_fmaf(d[st & 1][cb][i], sxr[st][i], acc[st % NACT][cb][i]);
+                // an empty statement that reads and writes the sums keeps the folds
+                // here, between the products, instead of all at the chunk's end
+                asm volatile("" : "+v"(acc[st % NACT][cb]));
+            }
+        };
+        static_for<NS>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int st = decltype(sc)::value;
+            constexpr int g = st / NACT;
+            constexpr int mb = st % NACT;
+            if constexpr (st + PF < NS) {
+                afr[st + PF] = frag(st + PF);
+                if constexpr (EXACT) sxr[st + PF] = sxv(st + PF);
+            }
+            if constexpr (mb == 0 && g < 3) dequant_step(sl, g + 1, (g & 1) ? bfa : bfb);
+            half8_t(&cur)[CB] = (g & 1) ? bfb : bfa;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                if constexpr (!EXACT)
+                    acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[st], cur[cb], acc[mb][cb], 0, 0, 0);
+                else
+                    d[st & 1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[st], cur[cb],
+                                                                           f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+            if constexpr (EXACT && st > 0) fold(std::integral_constant<int, st - 1>{});
+            // bf16: VALU work may move across products; exact: nothing does (the
+            // folds would otherwise sink past later products and hold their
+            // matrix-core results)
+            __builtin_amdgcn_sched_barrier(EXACT ? 0 : 0x0002);
+        });
+        if constexpr (EXACT) fold(std::integral_constant<int, NS - 1>{});
         }
     };
 
-    // prologue: weights of chunks 0..2 in flight, activation chunk 0 staged
-    Slot s0, s1, s2;
-    load_A(0);
-    load_B(0, s0);
-    load_B(min(1, nch - 1), s1);
-    load_B(min(2, nch - 1), s2);
-    store_A(0);
-    lds_barrier();
-
     // One chunk: stage the next activation chunk's loads, multiply the current
-    // one, refill this weight slot three chunks ahead, then write the staged
+    // one, refill this weight slot RING chunks ahead, then write the staged
     // chunk to the other LDS buffer (whose last readers finished before the
     // previous barrier).  Indices past the end are clamped: redundant in-bounds
-    // loads, and a staged buffer nobody reads.
+    // loads, and a staged buffer nobody reads.  Each instance issues its own
+    // prologue (weights of the first RING chunks in flight, activation chunk 0
+    // staged).  bf16 keeps three weight chunks in flight; exact mode, whose
+    // chunks are long (VALU folds), two, which keeps its registers within two
+    // waves per SIMD.
+    constexpr int RING = EXACT ? 2 : 3;
     auto main_loop = [&](auto nact) __attribute__((always_inline)) {
+        Slot sl[RING];
+        load_A(0);
+#pragma unroll
+        for (int i = 0; i < RING; ++i) load_B(min(i, nch - 1), sl[i]);
+        store_A(0);
+        lds_barrier();
         auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
             load_A(min(c + 1, nch - 1));
             __builtin_amdgcn_sched_barrier(0);
             compute(nact, c, cur);
             __builtin_amdgcn_sched_barrier(0);
-            load_B(min(c + 3, nch - 1), cur);
+            load_B(min(c + RING, nch - 1), cur);
             __builtin_amdgcn_sched_barrier(0);
             store_A((c + 1) & 1);
             lds_barrier();
         };
         int c = 0;
-        for (; c + 3 <= nch; c += 3) {
-            step(c, s0);
-            step(c + 1, s1);
-            step(c + 2, s2);
-        }
-        if (c < nch) step(c, s0);
-        if (c + 1 < nch) step(c + 1, s1);
+        for (; c + RING <= nch; c += RING)
+            static_for<RING>([&](auto ic) __attribute__((always_inline)) { step(c + decltype(ic)::value, sl[decltype(ic)::value]); });
+        static_for<RING - 1>([&](auto ic) __attribute__((always_inline)) {
+            if (c + decltype(ic)::value < nch) step(c + decltype(ic)::value, sl[decltype(ic)::value]);
+        });
     };
-    if constexpr (!EXACT && MB >= 8) {
-        main_loop(std::integral_constant<int, MB>{});
+    if constexpr (EXACT) {
+        static_for<MB>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int n = decltype(ic)::value + 1;
+            if (active_mb == n) main_loop(std::integral_constant<int, n>{});
+        });
     } else {
         main_loop(std::integral_constant<int, 0>{});
     }
@@ -517,6 +567,19 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
             }
         }
     }
+}
+
+template <int MODE, int OP, int MB, int CB>
+__global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
+    grouped_tile<MODE, OP, MB, CB>(a);
+}
+
+// Exact mode: register use capped at two waves per SIMD.  Under that cap the
+// compiler writes matrix-core results to ordinary VGPRs, where the VALU folds
+// read them (otherwise each fold first copies its operand out of an AGPR).
+template <int MODE, int OP, int MB, int CB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_grouped_exact(GroupedArgs a) {
+    grouped_tile<MODE, OP, MB, CB>(a);
 }
 
 // Large bf16 tiles on the 32x32x16 matrix-core shape (one wave per SIMD drives
@@ -980,8 +1043,11 @@ template <int MODE, int OP, int MB, int CB>
 void launch_tiles(GroupedArgs a, int S, hipStream_t st) {
     a.n_chunks = OP == 0 ? a.N / (32 * CB) : a.N / (64 * CB);
     const long tiles = ((long)S + (long)a.E * (16 * MB - 1)) / (16 * MB) + 1;
-    hipLaunchKernelGGL((k_grouped<MODE, OP, MB, CB>), dim3(8 * moe::per_xcd(tiles * a.n_chunks)), dim3(256), 0, st,
-                       a);
+    const dim3 grid(8 * moe::per_xcd(tiles * a.n_chunks));
+    if constexpr (MODE == MOE_MODE_EXACT_I8)
+        hipLaunchKernelGGL((k_grouped_exact<MODE, OP, MB, CB>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_grouped<MODE, OP, MB, CB>), grid, dim3(256), 0, st, a);
 }
 
 template <int OP, int M32>
