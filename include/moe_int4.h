@@ -60,7 +60,7 @@ typedef enum {
     MOE_ERR_LAUNCH = -4,      /* the HIP runtime rejected a kernel launch */
 } moe_status;
 
-enum { MOE_MODE_BF16 = 0, MOE_MODE_EXACT_I8 = 1 };
+enum { MOE_MODE_BF16 = 0, MOE_MODE_EXACT_I8 = 1, MOE_MODE_BF16_F16P = 2 };
 
 /* Version of this ABI (incremented on any signature change). */
 int moe_abi_version(void);
@@ -132,6 +132,18 @@ int moe_int4_prepack(const uint8_t* packed, const uint16_t* scale, int E, int N,
                      uint8_t* packed_out, uint16_t* scale_out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * fp16 staging format of activations (an implementation layout, not from the
+ * pages: the routed GEMMs run their operands as fp16 on the matrix cores, and
+ * their dequantised weights pair elements (p, p+4) of each 8-element block).
+ * out [rows, K] fp16 bits: for every row and block of 8 elements e0..e7 of x
+ * [rows, K] bf16, the block is stored as e0,e4,e1,e5,e2,e6,e3,e7, each
+ * converted bf16 -> fp16 rounding toward zero (exact in the fp16 normal
+ * range; larger magnitudes saturate to the largest finite fp16, as in the
+ * kernels' own conversion).  K a multiple of 8; buffers 16-byte aligned and
+ * not overlapping.  rows == 0 is a no-op. */
+int moe_act_f16p(const uint16_t* x, int rows, int K, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Grouped gate/up projections + SwiGLU over the ragged expert segments
  * ("Kimi exact-generator adaptation", "The preserved forward form";
  * "Kimi K2.5 donor reference", record "SwiGLU-style gated feed-forward
@@ -145,6 +157,12 @@ int moe_int4_prepack(const uint8_t* packed, const uint16_t* scale, int E, int N,
  *     G the exact int32 group dot product; h = silu(g) * u (fp32), quantised
  *     per row and group of 32 like moe_quant_act_int8 -> h = q_h [T*k, I]
  *     int8, h_scale = s_h [T*k, I/32] fp32.  Bit-exact.
+ *   mode MOE_MODE_BF16_F16P: the arithmetic of MOE_MODE_BF16 with the
+ *     activations already in the fp16 staging format of moe_act_f16p:
+ *     act = moe_act_f16p(x) [T,H], and h is written in that format (the
+ *     staging format of the bf16 h that MOE_MODE_BF16 writes).  Results are
+ *     bit-identical to MOE_MODE_BF16; the kernels skip the per-tile
+ *     conversion of the activations.
  * gate/up weights in the fragment layout of moe_int4_prepack.
  * Empty experts are skipped; rows of absent experts are not written. */
 int moe_int4_grouped_swiglu(int mode, const void* act, const float* act_scale,
@@ -158,6 +176,9 @@ int moe_int4_grouped_swiglu(int mode, const void* act, const float* act_scale,
  *   MOE_MODE_BF16: h [T*k, I] bf16 -> y [T*k, H] bf16 (= bf16 of the fp32 sum).
  *   MOE_MODE_EXACT_I8: h = q_h int8 with h_scale = s_h -> y [T*k, H] fp32,
  *     the fixed-order group combine as above.  Bit-exact.
+ *   MOE_MODE_BF16_F16P: h in the fp16 staging format (as written by
+ *     moe_int4_grouped_swiglu in that mode) -> y [T*k, H] bf16, bit-identical
+ *     to MOE_MODE_BF16 on the bf16 h. 
  * down weights in the fragment layout of moe_int4_prepack. */
 int moe_int4_grouped_down(int mode, const void* h, const float* h_scale, const uint8_t* down_packed,
                           const uint16_t* down_scale, const int32_t* offsets, int T, int k, int E,

@@ -213,6 +213,30 @@ __device__ __forceinline__ u32x4_t bf16x8_to_f16_perm(u32x4_t d) {
     return r;
 }
 
+// The fp16 staging format of activations (moe_act_f16p, mode
+// MOE_MODE_BF16_F16P): each 8-element block stored as e0,e4,e1,e5,e2,e6,e3,e7,
+// the pair order above.  Position of element `col` of a row in that format.
+__device__ __forceinline__ int f16p_col(int col) {
+    const int e = col & 7;
+    return (col & ~7) | (e < 4 ? 2 * e : 2 * e - 7);
+}
+
+// bf16 bits -> fp16 bits, rounding toward zero as the staging conversion does
+// (exact for bf16 values in the fp16 normal range).
+__device__ __forceinline__ uint16_t bf16_to_f16_bits(uint32_t b) {
+    return (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_bits_to_f32(b), 0.0f)) & 0xFFFFu);
+}
+
+// Store of a gate/up output element h (bf16 bits hb) at row-major index
+// row_base + col: bf16 as is, or in the fp16 staging format.
+template <bool F16P>
+__device__ __forceinline__ void store_h(void* out, size_t row_base, int col, uint32_t hb) {
+    if constexpr (F16P)
+        static_cast<uint16_t*>(out)[row_base + f16p_col(col)] = bf16_to_f16_bits(hb);
+    else
+        static_cast<uint16_t*>(out)[row_base + col] = (uint16_t)hb;
+}
+
 // 8 int8 (2 dwords, elements in order) -> 8 exact fp16 integers in pair order.
 __device__ __forceinline__ u32x4_t i8x8_to_f16_perm(uint32_t d0, uint32_t d1) {
     u32x4_t r;
@@ -248,9 +272,10 @@ __device__ __forceinline__ void lds_barrier() {
 template <int MODE, int OP, int MB, int CB>
 __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
     static_assert(CB == 2 || CB == 4, "column blocks per wave");
-    static_assert(CB == 4 || MODE == MOE_MODE_BF16, "exact mode quantises 32 output columns per wave");
+    static_assert(CB == 4 || MODE != MOE_MODE_EXACT_I8, "exact mode quantises 32 output columns per wave");
     constexpr int BM = 16 * MB;
     constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
+    constexpr bool F16P = MODE == MOE_MODE_BF16_F16P;  // activations already in the fp16 staging format
     constexpr bool GATEUP = OP == 0;
     // activation staging: a bf16 row chunk is 16 pieces of 16 B, an int8 row chunk 8
     constexpr int PIECES = EXACT ? 8 : 16;
@@ -353,7 +378,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
             const int row = srow_of(it);
             const int piece = lane % PIECES;
             if (!EXACT) {
-                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = bf16x8_to_f16_perm(Aq[it]);
+                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = F16P ? Aq[it] : bf16x8_to_f16_perm(Aq[it]);
             } else {
                 *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16]) = i8x8_to_f16_perm(Aq[it][0], Aq[it][1]);
                 *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16 + 8]) = i8x8_to_f16_perm(Aq[it][2], Aq[it][3]);
@@ -529,7 +554,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
                         const uint32_t ub = f32_to_bf16_bits(acc[mb][CB / 2 + p][i]);
                         const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
                         const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
-                        if (ok) static_cast<uint16_t*>(a.out)[orow * N + n0 + 16 * p + r] = (uint16_t)hb;
+                        if (ok) store_h<F16P>(a.out, orow * N, n0 + 16 * p + r, hb);
                     }
                 } else {
                     const float h0 = moe_silu(acc[mb][0][i]) * acc[mb][CB / 2][i];
@@ -592,7 +617,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // dword g of the first holds K step 2g, of the second step 2g + 1.  The
 // accumulator element i of lane l is row 8(i/4) + 4 kb + i%4, column c.
 // Staging, barrier and weight ring as in k_grouped.
-template <int OP, int M32>
+template <int OP, int M32, bool F16P>
 __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
     constexpr int BM = 32 * M32;
     constexpr bool GATEUP = OP == 0;
@@ -669,7 +694,7 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
     };
     auto store_piece = [&](int it, int buf) __attribute__((always_inline)) {
         *reinterpret_cast<u32x4_t*>(&As[buf][A_ITERS * 4 * wave + 4 * it + (lane >> 4)][(lane & 15) * 8]) =
-            bf16x8_to_f16_perm(Aq[it]);
+            F16P ? Aq[it] : bf16x8_to_f16_perm(Aq[it]);
     };
     auto load_A = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
@@ -792,7 +817,7 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
                 const uint32_t ub = f32_to_bf16_bits(acc[mb][1][i]);
                 const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
                 const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
-                static_cast<uint16_t*>(a.out)[orow * N + n0 + c32] = (uint16_t)hb;
+                store_h<F16P>(a.out, orow * N, n0 + c32, hb);
             } else {
 #pragma unroll
                 for (int cb = 0; cb < 2; ++cb)
@@ -815,6 +840,7 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
 template <int MODE, int OP, int D>
 __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
     constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
+    constexpr bool F16P = MODE == MOE_MODE_BF16_F16P;  // activations already in the fp16 staging format
     constexpr bool GATEUP = OP == 0;
 
     TileInfo ti;
@@ -892,7 +918,8 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
             half8_t af;
             f32x4_t sx;
             if (!EXACT) {
-                af = __builtin_bit_cast(half8_t, bf16x8_to_f16_perm(avalid ? sl.A[g] : u32x4_t{0u, 0u, 0u, 0u}));
+                const u32x4_t av = avalid ? sl.A[g] : u32x4_t{0u, 0u, 0u, 0u};
+                af = __builtin_bit_cast(half8_t, F16P ? av : bf16x8_to_f16_perm(av));
             } else {
                 af = __builtin_bit_cast(half8_t, i8x8_to_f16_perm(avalid ? sl.A[g][0] : 0u, avalid ? sl.A[g][1] : 0u));
 #pragma unroll
@@ -948,7 +975,7 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
                     const uint32_t ub = f32_to_bf16_bits(acc[2 + p][i]);
                     const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
                     const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
-                    if (ok) static_cast<uint16_t*>(a.out)[orow * N + n0 + 16 * p + r] = (uint16_t)hb;
+                    if (ok) store_h<F16P>(a.out, orow * N, n0 + 16 * p + r, hb);
                 }
             } else {
                 const float h0 = moe_silu(acc[0][i]) * acc[2][i];
@@ -1017,6 +1044,12 @@ __global__ __launch_bounds__(256) void k_prepack_s(const uint16_t* __restrict__ 
     *reinterpret_cast<u32x2_t*>(dst + (size_t)t * 4) = v;
 }
 
+// Activations into the fp16 staging format: one 8-element block per thread.
+__global__ __launch_bounds__(256) void k_act_f16p(const u32x4_t* __restrict__ x, u32x4_t* __restrict__ out, long blocks) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < blocks) out[i] = bf16x8_to_f16_perm(x[i]);
+}
+
 constexpr int kSkinnyDepth = 4;       // chunk slots of the decode kernel (D-1 chunks in flight)
 constexpr int kSkinnyDepthExact = 3;  // exact mode carries the activation scales too
 
@@ -1037,7 +1070,7 @@ int pick_mb(int S, int E) {
 // whose accumulators then leave room for more than one workgroup per CU; the
 // 12-block tiles keep 4 (halving them doubles the LDS fragment reads per product
 // and measured slower).
-constexpr int pick_cb(int mode, int mb) { return (mode == MOE_MODE_BF16 && mb >= 6 && mb < 12) ? 2 : 4; }
+constexpr int pick_cb(int mode, int mb) { return (mode != MOE_MODE_EXACT_I8 && mb >= 6 && mb < 12) ? 2 : 4; }
 
 template <int MODE, int OP, int MB, int CB>
 void launch_tiles(GroupedArgs a, int S, hipStream_t st) {
@@ -1050,11 +1083,12 @@ void launch_tiles(GroupedArgs a, int S, hipStream_t st) {
         hipLaunchKernelGGL((k_grouped<MODE, OP, MB, CB>), grid, dim3(256), 0, st, a);
 }
 
-template <int OP, int M32>
+template <int MODE, int OP, int M32>
 void launch_tiles32(GroupedArgs a, int S, hipStream_t st) {
     a.n_chunks = OP == 0 ? a.N / 128 : a.N / 256;
     const long tiles = ((long)S + (long)a.E * (32 * M32 - 1)) / (32 * M32) + 1;
-    hipLaunchKernelGGL((k_grouped32<OP, M32>), dim3(8 * moe::per_xcd(tiles * a.n_chunks)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_grouped32<OP, M32, MODE == MOE_MODE_BF16_F16P>), dim3(8 * moe::per_xcd(tiles * a.n_chunks)),
+                       dim3(256), 0, st, a);
 }
 
 template <int MODE, int OP>
@@ -1084,8 +1118,8 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
             const size_t act_bytes = act_rows * (size_t)a.K * 2;
             a.act_bytes = (uint32_t)act_bytes;
             if (act_bytes >= ((size_t)1 << 32)) launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st);
-            else if (mb == 8) launch_tiles32<OP, 4>(a, S, st);
-            else launch_tiles32<OP, 6>(a, S, st);
+            else if (mb == 8) launch_tiles32<MODE, OP, 4>(a, S, st);
+            else launch_tiles32<MODE, OP, 6>(a, S, st);
             break;
         }
         }
@@ -1095,7 +1129,7 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
 
 int check_common(const char* what, int mode, int T, int k, int E) {
     using namespace moe;
-    if (mode != MOE_MODE_BF16 && mode != MOE_MODE_EXACT_I8)
+    if (mode != MOE_MODE_BF16 && mode != MOE_MODE_EXACT_I8 && mode != MOE_MODE_BF16_F16P)
         return fail(MOE_ERR_INVALID_ARG, "%s: mode %d", what, mode);
     if (T < 0 || k <= 0 || E <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes", what);
     if (E > 1024 || k > 16 || k > E || (long)T * k >= (1L << 31))
@@ -1143,8 +1177,9 @@ extern "C" int moe_int4_grouped_swiglu(int mode, const void* act, const float* a
     a.out = h;
     a.out_scale = h_scale;
     hipStream_t st = as_stream(stream);
-    return exact ? launch_grouped<MOE_MODE_EXACT_I8, 0>(a, T * k, st, what)
-                 : launch_grouped<MOE_MODE_BF16, 0>(a, T * k, st, what);
+    if (exact) return launch_grouped<MOE_MODE_EXACT_I8, 0>(a, T * k, st, what);
+    if (mode == MOE_MODE_BF16_F16P) return launch_grouped<MOE_MODE_BF16_F16P, 0>(a, T * k, st, what);
+    return launch_grouped<MOE_MODE_BF16, 0>(a, T * k, st, what);
 }
 
 extern "C" int moe_int4_grouped_down(int mode, const void* h, const float* h_scale,
@@ -1176,8 +1211,27 @@ extern "C" int moe_int4_grouped_down(int mode, const void* h, const float* h_sca
     a.N = H;
     a.out = y;
     hipStream_t st = as_stream(stream);
-    return exact ? launch_grouped<MOE_MODE_EXACT_I8, 1>(a, T * k, st, what)
-                 : launch_grouped<MOE_MODE_BF16, 1>(a, T * k, st, what);
+    if (exact) return launch_grouped<MOE_MODE_EXACT_I8, 1>(a, T * k, st, what);
+    if (mode == MOE_MODE_BF16_F16P) return launch_grouped<MOE_MODE_BF16_F16P, 1>(a, T * k, st, what);
+    return launch_grouped<MOE_MODE_BF16, 1>(a, T * k, st, what);
+}
+
+extern "C" int moe_act_f16p(const uint16_t* x, int rows, int K, uint16_t* out, void* stream) {
+    using namespace moe;
+    const char* what = "moe_act_f16p";
+    if (rows < 0 || K <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes rows=%d K=%d", what, rows, K);
+    if (K % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: K=%d (multiple of 8)", what, K);
+    if (rows == 0) return MOE_OK;
+    if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    if (!aligned16(x) || !aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", what);
+    const char* xb = reinterpret_cast<const char*>(x);
+    const char* ob = reinterpret_cast<const char*>(out);
+    const size_t bytes = (size_t)rows * (size_t)K * 2;
+    if (xb < ob + bytes && ob < xb + bytes) return fail(MOE_ERR_INVALID_ARG, "%s: input and output overlap", what);
+    const long blocks = (long)rows * (K / 8);
+    hipLaunchKernelGGL(k_act_f16p, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, as_stream(stream),
+                       reinterpret_cast<const u32x4_t*>(x), reinterpret_cast<u32x4_t*>(out), blocks);
+    return launch_status(what);
 }
 
 extern "C" int moe_int4_prepack(const uint8_t* packed, const uint16_t* scale, int E, int N, int K,

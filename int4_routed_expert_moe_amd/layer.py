@@ -44,6 +44,9 @@ class MoELayer:
     permuted once into the fragment layout here."""
 
     SIDE_STREAM_MIN_T = 1024  # tokens from which the shared expert runs on its own stream
+    # tokens from which the bf16 expert input is converted once to the fp16 staging
+    # format (instead of by every tile of the grouped GEMMs)
+    STAGED_ACT_MIN_T = 256
 
     def __init__(self, cfg: dict, router_w, router_b, experts: dict, shared: dict | None = None,
                  latent: dict | None = None):
@@ -90,6 +93,7 @@ class MoELayer:
         dev, E, k, H, I, Kin = self.device, self.E, self.k, self.H, self.I, self.Kin
         S = T * k
         exact = self.mode == _m.MOE_MODE_EXACT_I8
+        staged = not exact and T >= self.STAGED_ACT_MIN_T
         w = {
             "route_ws": torch.empty(max(1, _m.moe_route_workspace_bytes(T, self.H, E)), dtype=torch.uint8, device=dev),
             "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
@@ -98,11 +102,14 @@ class MoELayer:
             "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
             "sorted_slot": torch.empty(S, dtype=torch.int32, device=dev),
             "slot_pos": torch.empty(S, dtype=torch.int32, device=dev),
-            "h": torch.empty((S, I), dtype=torch.int8 if exact else torch.bfloat16, device=dev),
+            "h": torch.empty((S, I), dtype=torch.int8 if exact else torch.float16 if staged else torch.bfloat16,
+                             device=dev),
             "h_scale": torch.empty((S, I // 32), dtype=torch.float32, device=dev) if exact else None,
             "y": torch.empty((S, Kin), dtype=torch.float32 if exact else torch.bfloat16, device=dev),
             "out": torch.empty((T, H), dtype=torch.float32 if exact else torch.bfloat16, device=dev),
         }
+        if staged:
+            w["act16"] = torch.empty((T, Kin), dtype=torch.float16, device=dev)
         if exact:
             w["qx"] = torch.empty((T, Kin), dtype=torch.int8, device=dev)
             w["sx"] = torch.empty((T, Kin // 32), dtype=torch.float32, device=dev)
@@ -182,11 +189,21 @@ class MoELayer:
             mark("moe_quant_act_int8")
             _m.moe_int4_grouped_swiglu(self.mode, w["qx"], w["sx"], ex["wg"], ex["sg"], ex["wu"], ex["su"],
                                        w["offsets"], w["sorted_slot"], T, k, E, Kin, I, w["h"], w["h_scale"])
+            gmode = self.mode
+        elif "act16" in w:
+            # bf16 arithmetic on activations converted once to the fp16 staging
+            # format; h stays in that format between the two grouped calls
+            _m.moe_act_f16p(act, w["act16"])
+            mark("moe_act_f16p")
+            gmode = _m.MOE_MODE_BF16_F16P
+            _m.moe_int4_grouped_swiglu(gmode, w["act16"], None, ex["wg"], ex["sg"], ex["wu"], ex["su"],
+                                       w["offsets"], w["sorted_slot"], T, k, E, Kin, I, w["h"], None)
         else:
-            _m.moe_int4_grouped_swiglu(self.mode, act, None, ex["wg"], ex["sg"], ex["wu"], ex["su"],
+            gmode = self.mode
+            _m.moe_int4_grouped_swiglu(gmode, act, None, ex["wg"], ex["sg"], ex["wu"], ex["su"],
                                        w["offsets"], w["sorted_slot"], T, k, E, Kin, I, w["h"], None)
         mark("moe_int4_grouped_swiglu")
-        _m.moe_int4_grouped_down(self.mode, w["h"], w["h_scale"], ex["wd"], ex["sd"], w["offsets"], T, k, E, I,
+        _m.moe_int4_grouped_down(gmode, w["h"], w["h_scale"], ex["wd"], ex["sd"], w["offsets"], T, k, E, I,
                                  Kin, w["y"])
         mark("moe_int4_grouped_down")
         if side is not None:

@@ -29,6 +29,7 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_LAUNCH = -4
 MOE_MODE_BF16 = 0
 MOE_MODE_EXACT_I8 = 1
+MOE_MODE_BF16_F16P = 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -43,6 +44,7 @@ EXPORTS = {
     "moe_permute": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "moe_quant_act_int8": ([_P, _I, _I, _P, _P, _P], _I),
     "moe_int4_prepack": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
+    "moe_act_f16p": ([_P, _I, _I, _P, _P], _I),
     "moe_int4_grouped_swiglu": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_int4_grouped_down": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_I, _P, _P, _P, _P, _I, _I, _I, _P, _P], _I),
@@ -148,9 +150,23 @@ def moe_int4_prepack(packed, scale, packed_out, scale_out):
                                                      _ptr(scale_out), _stream()))
 
 
+_ACT_DTYPE = {MOE_MODE_BF16: torch.bfloat16, MOE_MODE_EXACT_I8: torch.int8, MOE_MODE_BF16_F16P: torch.float16}
+
+
+def moe_act_f16p(x, out):
+    """x [rows, K] bf16 -> out [rows, K] fp16 in the staging format of the routed GEMMs
+    (8-element blocks stored as e0,e4,e1,e5,e2,e6,e3,e7)."""
+    if x.dim() != 2:
+        raise ValueError("x: expected a 2-D tensor")
+    rows, K = x.shape
+    _need(x, torch.bfloat16, (rows, K), "x")
+    _need(out, torch.float16, (rows, K), "out")
+    _check("moe_act_f16p", _lib.moe_act_f16p(_ptr(x), rows, K, _ptr(out), _stream()))
+
+
 def moe_int4_grouped_swiglu(mode, act, act_scale, gate_packed, gate_scale, up_packed, up_scale, offsets,
                             sorted_slot, T, k, E, H, I, h, h_scale):
-    _need(act, torch.bfloat16 if mode == MOE_MODE_BF16 else torch.int8, (T, H), "act")
+    _need(act, _ACT_DTYPE.get(mode, torch.bfloat16), (T, H), "act")
     for t, dt, shp, nm in ((gate_packed, torch.uint8, (E, I, H // 2), "gate_packed"),
                            (gate_scale, torch.bfloat16, (E, I, H // 32), "gate_scale"),
                            (up_packed, torch.uint8, (E, I, H // 2), "up_packed"),
@@ -158,8 +174,8 @@ def moe_int4_grouped_swiglu(mode, act, act_scale, gate_packed, gate_scale, up_pa
                            (offsets, torch.int32, (E + 1,), "offsets"),
                            (sorted_slot, torch.int32, (T * k,), "sorted_slot")):
         _need(t, dt, shp, nm)
-    if mode == MOE_MODE_BF16:
-        _need(h, torch.bfloat16, (T * k, I), "h")
+    if mode != MOE_MODE_EXACT_I8:
+        _need(h, _ACT_DTYPE.get(mode, torch.bfloat16), (T * k, I), "h")
     else:
         _need(act_scale, torch.float32, (T, H // 32), "act_scale")
         _need(h, torch.int8, (T * k, I), "h")
@@ -170,11 +186,11 @@ def moe_int4_grouped_swiglu(mode, act, act_scale, gate_packed, gate_scale, up_pa
 
 
 def moe_int4_grouped_down(mode, h, h_scale, down_packed, down_scale, offsets, T, k, E, I, H, y):
-    _need(h, torch.bfloat16 if mode == MOE_MODE_BF16 else torch.int8, (T * k, I), "h")
+    _need(h, _ACT_DTYPE.get(mode, torch.bfloat16), (T * k, I), "h")
     _need(down_packed, torch.uint8, (E, H, I // 2), "down_packed")
     _need(down_scale, torch.bfloat16, (E, H, I // 32), "down_scale")
     _need(offsets, torch.int32, (E + 1,), "offsets")
-    if mode == MOE_MODE_BF16:
+    if mode != MOE_MODE_EXACT_I8:
         _need(y, torch.bfloat16, (T * k, H), "y")
     else:
         _need(h_scale, torch.float32, (T * k, I // 32), "h_scale")

@@ -55,6 +55,30 @@ def np_bf16(t):
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+_F16P_ORDER = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+
+
+def f16p_values(bits16):
+    """fp16 staging format (8-element blocks stored as e0,e4,e1,e5,e2,e6,e3,e7)
+    -> float64 in element order."""
+    h = np.asarray(bits16, np.uint16).view(np.float16).astype(np.float64)
+    blocks = h.reshape(*h.shape[:-1], h.shape[-1] // 8, 8)
+    out = np.empty_like(blocks)
+    out[..., _F16P_ORDER] = blocks
+    return out.reshape(h.shape)
+
+
+def act_bits_bf16(t):
+    """A bf16-path activation buffer as bf16 bit patterns in element order: bf16
+    as is, or the fp16 staging format (whose values are bf16 values, so the
+    conversion back is exact in the fp16 normal range)."""
+    if t.dtype == torch.float16:
+        from tests import refmath
+        v = f16p_values(t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+        return refmath.bf16_from_f32(v.astype(np.float32))
+    return np_bf16(t)
+
+
 def bf16_to_f64(a):
     return ((np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
 

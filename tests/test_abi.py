@@ -107,4 +107,12 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert _status(lib, pp, fake, fake, 2, 32, 256, fake, P(0x200000), null) == -1
     assert _status(lib, pp, fake, P(0x3004), 2, 32, 256, P(0x100000), P(0x200000), null) == -1
     assert _status(lib, pp, null, null, 0, 32, 256, null, null, null) == 0
+    # staging conversion: K not a multiple of 8, null pointer, overlap, zero rows
+    assert _status(lib, "moe_act_f16p", fake, 4, 12, P(0x200000), null) == -2
+    assert _status(lib, "moe_act_f16p", null, 4, 16, P(0x200000), null) == -1
+    assert _status(lib, "moe_act_f16p", P(0x100000), 4, 16, P(0x100010), null) == -1
+    assert _status(lib, "moe_act_f16p", null, 0, 16, null, null) == 0
+    # grouped calls accept the staging-format mode and reject others
+    assert _status(lib, g, 3, fake, null, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
+    assert _status(lib, g, 2, fake, fake, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
     assert lib.moe_status_string(-3) == b"workspace missing or too small"

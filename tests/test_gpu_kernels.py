@@ -6,7 +6,8 @@ import torch
 
 import oracle
 from tests import refmath
-from tests.gpu_common import (assert_bf16_close, assert_f32_close, bf16_dev, np_bf16, say)
+from tests.gpu_common import (assert_bf16_close, assert_f32_close, bf16_dev, bf16_to_f64, f16p_values, np_bf16,
+                              say)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +22,21 @@ def m():
 
 def _rand_bf16(g, shape, std=1.0):
     return refmath.bf16_from_f32((g.standard_normal(shape) * std).astype(np.float32))
+
+
+_F16P_ORDER = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+
+
+def _f16p_ref(bits):
+    """The fp16 staging format from its definition: bf16 -> fp16 rounding toward
+    zero (saturating at the largest finite fp16), each 8-element block stored as
+    e0,e4,e1,e5,e2,e6,e3,e7.  Returns fp16 bit patterns."""
+    f = bf16_to_f64(bits)
+    h = f.astype(np.float16)                       # nearest
+    over = np.abs(h.astype(np.float64)) > np.abs(f)  # rounded away from zero (or to inf)
+    h[over] = np.nextafter(h[over], np.float16(0))
+    h = h.reshape(*bits.shape[:-1], bits.shape[-1] // 8, 8)[..., _F16P_ORDER]
+    return h.reshape(bits.shape).view(np.uint16)
 
 
 def _packed(g, shape):
@@ -230,6 +246,26 @@ def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     torch.cuda.synchronize()
     assert_bf16_close(np_bf16(h), ref["h"], "h")
     assert_bf16_close(np_bf16(y), ref["y"], "y")
+    # the fp16 staging-format mode: against the oracle, and bit-identical to the bf16 mode
+    say(f"grouped bf16 (fp16 staging format) T={T} H={H} I={I} E={E} k={k}")
+    xp = torch.empty((T, H), dtype=torch.float16, device="cuda")
+    m.moe_act_f16p(bf16_dev(x), xp)
+    h2 = torch.empty((S, I), dtype=torch.float16, device="cuda")
+    m.moe_int4_grouped_swiglu(m.MOE_MODE_BF16_F16P, xp, None, D["wg"], D["sg"], D["wu"], D["su"], off_d,
+                              torch.from_numpy(ss).cuda(), T, k, E, H, I, h2, None)
+    hp_ref = torch.empty((S, I), dtype=torch.float16, device="cuda")
+    m.moe_act_f16p(bf16_dev(ref["h"]), hp_ref)
+    y2 = torch.empty((S, H), dtype=torch.bfloat16, device="cuda")
+    m.moe_int4_grouped_down(m.MOE_MODE_BF16_F16P, hp_ref, None, D["wd"], D["sd"], off_d, T, k, E, I, H, y2)
+    torch.cuda.synchronize()
+    h2_bits = h2.view(torch.int16).cpu().numpy().view(np.uint16)
+    got_h = f16p_values(h2_bits)
+    ref_h = bf16_to_f64(ref["h"])
+    scale = np.sqrt(np.mean(ref_h ** 2)) + 1e-30
+    assert np.all(np.abs(got_h - ref_h) <= 1e-2 * scale + 2e-2 * np.abs(ref_h)), "h (staging format)"
+    np.testing.assert_array_equal(h2_bits, _f16p_ref(np_bf16(h)))
+    assert_bf16_close(np_bf16(y2), ref["y"], "y (staging format)")
+    np.testing.assert_array_equal(np_bf16(y2), np_bf16(y))
     # combine on the GPU's y vs the oracle combine of the same y
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     shared = _rand_bf16(g, (T, H))
@@ -278,6 +314,23 @@ def test_grouped_exact_bitexact(m, T, H, I, E, k, skew, seed):
     torch.cuda.synchronize()
     ref_out = oracle.combine_f32(ref["y"][sp].reshape(T, k, H), w)
     np.testing.assert_array_equal(out.cpu().numpy(), ref_out)
+
+
+@pytest.mark.parametrize("rows,K,seed", [(1, 8, 0), (37, 7168, 1), (300, 2048, 2)])
+def test_act_f16p_layout(m, rows, K, seed):
+    """The staging conversion against its definition, bit for bit, with values
+    below the fp16 normal range, above its largest finite value, and signed zeros."""
+    say(f"act_f16p rows={rows} K={K}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (rows, K), std=4.0)
+    flat = x.reshape(-1)
+    special = refmath.bf16_from_f32(np.array([1e-6, -3e-5, 7e4, -1e6, 0.0, -0.0, 65504.0, 2.0 ** -14],
+                                             dtype=np.float32))
+    flat[: min(flat.size, special.size)] = special[: min(flat.size, special.size)]
+    out = torch.empty((rows, K), dtype=torch.float16, device="cuda")
+    m.moe_act_f16p(bf16_dev(x), out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), _f16p_ref(x))
 
 
 # ---------------------------------------------------------------- dense pieces

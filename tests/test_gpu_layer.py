@@ -11,7 +11,8 @@ import torch
 
 import oracle
 from int4_routed_expert_moe_amd import synthetic
-from tests.gpu_common import (assert_bf16_close, assert_f32_close, bf16_dev, inputs, layer, np_bf16, say)
+from tests.gpu_common import (act_bits_bf16, assert_bf16_close, assert_f32_close, bf16_dev, inputs, layer, np_bf16,
+                              say)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,7 +71,7 @@ def test_layer_parity(cfg_id):
         assert_f32_close(got, ref, "exact out", 1e-5)
         np.testing.assert_array_equal(got, ref)
     else:
-        assert_bf16_close(np_bf16(ws["h"])[pos], inter["h"], "h")
+        assert_bf16_close(act_bits_bf16(ws["h"])[pos], inter["h"], "h")
         if cfg.get("L"):
             assert_bf16_close(np_bf16(ws["x_lat"])[toks], inter["x_lat"], "x_lat")
             assert_bf16_close(np_bf16(ws["routed"])[toks], inter["routed"], "routed")
