@@ -361,20 +361,31 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
     };
     u32x4_t Aq[A_ITERS];
     f32x4_t SXq = {0.f, 0.f, 0.f, 0.f};
-    auto load_A = [&](int c) __attribute__((always_inline)) {
+    // With NACT > 0 active row blocks known at compile time, staging instructions
+    // whose rows all lie past them are skipped (wave-uniform branches): their
+    // rows are never read.
+    auto staged = [&](auto nact, int it) __attribute__((always_inline)) {
+        constexpr int NACT = decltype(nact)::value;
+        return NACT == 0 || A_ITERS * RPI * wave + RPI * it < 16 * NACT;
+    };
+    auto load_A = [&](int c, auto nact) __attribute__((always_inline)) {
+        constexpr int NACT = decltype(nact)::value;
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
+            if (!staged(nact, it)) continue;
             if (!EXACT)
                 Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + aoff[it] + c * kKC);
             else
                 Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + aoff[it] + c * kKC);
         }
-        if (EXACT && tid < BM)
+        if (EXACT && tid < (NACT > 0 ? 16 * NACT : BM))
             SXq = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)sxrow * (K / 32) + c * 4);
     };
-    auto store_A = [&](int buf) __attribute__((always_inline)) {
+    auto store_A = [&](int buf, auto nact) __attribute__((always_inline)) {
+        constexpr int NACT = decltype(nact)::value;
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
+            if (!staged(nact, it)) continue;
             const int row = srow_of(it);
             const int piece = lane % PIECES;
             if (!EXACT) {
@@ -384,7 +395,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
                 *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16 + 8]) = i8x8_to_f16_perm(Aq[it][2], Aq[it][3]);
             }
         }
-        if (EXACT && tid < BM) {
+        if (EXACT && tid < (NACT > 0 ? 16 * NACT : BM)) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) SXs[buf][g][tid] = SXq[g];
         }
@@ -505,19 +516,19 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
     constexpr int RING = EXACT ? 2 : 3;
     auto main_loop = [&](auto nact) __attribute__((always_inline)) {
         Slot sl[RING];
-        load_A(0);
+        load_A(0, nact);
 #pragma unroll
         for (int i = 0; i < RING; ++i) load_B(min(i, nch - 1), sl[i]);
-        store_A(0);
+        store_A(0, nact);
         lds_barrier();
         auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
-            load_A(min(c + 1, nch - 1));
+            load_A(min(c + 1, nch - 1), nact);
             __builtin_amdgcn_sched_barrier(0);
             compute(nact, c, cur);
             __builtin_amdgcn_sched_barrier(0);
             load_B(min(c + RING, nch - 1), cur);
             __builtin_amdgcn_sched_barrier(0);
-            store_A((c + 1) & 1);
+            store_A((c + 1) & 1, nact);
             lds_barrier();
         };
         int c = 0;
