@@ -16,11 +16,14 @@
 // Decode-shaped problems (few rows) split K over the grid and write fp32
 // partials that a second kernel sums in a fixed order (deterministic), then
 // applies the epilogue.
+#include <utility>
+
 #include "moe_common.h"
 
 namespace {
 
 constexpr int kDKC = 128;
+constexpr int kDense32MinM = 256;  // rows from which the 32x32 tile kernel runs
 constexpr int kDAStride = 136;  // bf16 per LDS row
 
 enum { EPI_LINEAR = 0, EPI_SWIGLU = 1 };
@@ -232,6 +235,172 @@ __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
     }
 }
 
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled whatever the body's size.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Row tiles of 32*M32 rows on v_mfma_f32_32x32x16_bf16 (one wave per SIMD
+// drives that shape near its peak; the 16x16x32 shape above stops near 1.4 PF
+// at this occupancy).  A workgroup is 4 waves; each wave owns two 32-column
+// blocks (linear: 64 output columns; swiglu: 32 gate and the same 32 up
+// columns) and all tile rows.  Within a 128-wide K chunk lane (c, kb) holds K
+// elements [64 kb, 64 kb + 64) of its row or column in 8 steps of 8 (both
+// operands use the same order, so each step still multiplies matching K):
+// every weight load then reads whole 128-byte lines, and the A-fragment reads
+// from LDS (272-byte rows) are free of bank conflicts.  The A tile is staged in
+// LDS one chunk ahead, a piece every 4 products; weights run one chunk ahead
+// in a 2-slot register ring; one LDS-only barrier per chunk.  Accumulator
+// element i of lane l is row 8(i/4) + 4 kb + i%4, column c.
+template <int M32, int EPI>
+__global__ __launch_bounds__(256) void k_dense32(DenseArgs a) {
+    constexpr int BM = 32 * M32;
+    constexpr int A_ITERS = BM * 16 / 256;  // 16-byte pieces per lane per chunk
+    constexpr int NS = 8 * M32;             // (K step, row block) products per chunk
+    static_assert(NS == 4 * A_ITERS, "staging: one piece every 4 products");
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][kDAStride];
+
+    const long L = xcd_logical_block(a.per_xcd);
+    if (L >= a.n_logical) return;
+    const int nc = (int)(L % a.n_chunks);
+    const int tm = (int)(L / a.n_chunks);
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int c32 = lane & 31;
+    const int kb = lane >> 5;
+    const int K = a.K;
+    const int m0 = tm * BM;
+    const int rows = min(BM, a.M - m0);
+    const int nch = K / kDKC;
+
+    // weight rows past N read the last row (never stored)
+    const int n0 = EPI == EPI_SWIGLU ? nc * 128 + wave * 32 : nc * 256 + wave * 64;
+    const uint16_t* wrow[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int n = min(EPI == EPI_SWIGLU ? n0 + c32 : n0 + 32 * cb + c32, a.N0 - 1);
+        wrow[cb] = (EPI == EPI_SWIGLU && cb == 1 ? a.w1 : a.w0) + (size_t)n * K + 64 * kb;
+    }
+
+    // A staging: each wave load instruction reads 4 whole row chunks (16 lanes x
+    // 16 contiguous bytes); wave w moves rows 4*A_ITERS*w + 4*it + lane/16 (rows
+    // past the tile read the tile's first row; their products are never stored)
+    auto srow_of = [&](int it) { return 4 * A_ITERS * wave + 4 * it + (lane >> 4); };
+    uint32_t aoff[A_ITERS];
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it)
+        aoff[it] = (uint32_t)((m0 + (srow_of(it) < rows ? srow_of(it) : 0)) * K + (lane & 15) * 8);
+    u32x4_t Aq[A_ITERS];
+    auto load_piece = [&](int it, int c) __attribute__((always_inline)) {
+        Aq[it] = *reinterpret_cast<const u32x4_t*>(a.x + aoff[it] + (size_t)c * kDKC);
+    };
+    auto store_piece = [&](int it, int buf) __attribute__((always_inline)) {
+        *reinterpret_cast<u32x4_t*>(&As[buf][srow_of(it)][(lane & 15) * 8]) = Aq[it];
+    };
+
+    struct Slot {
+        u32x4_t B[2][8];  // per column block and step: 8 bf16 of the lane's weight row
+    };
+    auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                sl.B[cb][q] = *reinterpret_cast<const u32x4_t*>(wrow[cb] + (size_t)c * kDKC + 8 * q);
+    };
+
+    f32x16_t acc[M32][2];
+#pragma unroll
+    for (int mb = 0; mb < M32; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][cb][i] = 0.0f;
+
+    auto compute = [&](int c, const Slot& sl) __attribute__((always_inline)) {
+        const int buf = c & 1;
+        constexpr int PF = 4;
+        auto frag = [&](int p) __attribute__((always_inline)) {
+            return __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(&As[buf][32 * (p % M32) + c32][64 * kb + 8 * (p / M32)]));
+        };
+        bf16x8_t afr[NS];
+#pragma unroll
+        for (int q = 0; q < PF; ++q) afr[q] = frag(q);
+        static_for<NS>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int p = decltype(pc)::value;
+            constexpr int st = p / M32;
+            constexpr int mb = p % M32;
+            if constexpr (p + PF < NS) afr[p + PF] = frag(p + PF);
+            if constexpr (p % 4 == 2) {
+                store_piece(p / 4, (c + 1) & 1);
+                load_piece(p / 4, min(c + 2, nch - 1));
+            }
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    afr[p], __builtin_bit_cast(bf16x8_t, sl.B[cb][st]), acc[mb][cb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0x0002);
+        });
+    };
+
+    // prologue: the loads in flight at each step's start are, in issue order,
+    // weights c, activations c+1, weights c+1
+    Slot s0, s1;
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) load_piece(it, 0);
+    load_B(0, s0);
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) store_piece(it, 0);
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) load_piece(it, min(1, nch - 1));
+    load_B(min(1, nch - 1), s1);
+    lds_barrier();
+    auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
+        compute(c, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        load_B(min(c + 2, nch - 1), cur);
+        lds_barrier();
+    };
+    int c = 0;
+    for (; c + 2 <= nch; c += 2) {
+        step(c, s0);
+        step(c + 1, s1);
+    }
+    if (c < nch) step(c, s0);
+
+#pragma unroll
+    for (int mb = 0; mb < M32; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
+            if (rl >= rows) continue;
+            const size_t m = (size_t)(m0 + rl);
+            if (EPI == EPI_SWIGLU) {
+                const int col = n0 + c32;
+                if (col < a.N0) a.y[m * a.N0 + col] = (uint16_t)silu_mul_bits(acc[mb][0][i], acc[mb][1][i]);
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb) {
+                    const int col = n0 + 32 * cb + c32;
+                    if (col < a.N0) {
+                        uint32_t yb = f32_to_bf16_bits(acc[mb][cb][i]);
+                        if (a.add) yb = add_bits(yb, a.add[m * a.N0 + col]);
+                        a.y[m * a.N0 + col] = (uint16_t)yb;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Sum the split-K partials in ascending split order, then the epilogue.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_dense_reduce(const float* __restrict__ part, int ksplit, int M,
@@ -335,6 +504,26 @@ int run_dense(int epi, const uint16_t* x, const uint16_t* w0, const uint16_t* w1
         const dim3 g((unsigned)((n + 255) / 256));
         if (sw) hipLaunchKernelGGL(k_dense_reduce<EPI_SWIGLU>, g, dim3(256), 0, st, a.part, p.ksplit, M, N0, Ntot, nullptr, y);
         else hipLaunchKernelGGL(k_dense_reduce<EPI_LINEAR>, g, dim3(256), 0, st, a.part, p.ksplit, M, N0, Ntot, add, y);
+        return moe::launch_status(what);
+    }
+    if (M >= kDense32MinM) {
+        // 32x32 tiles of 128 rows (the weights, read from L2 once per row tile,
+        // dominate a tile's operand traffic: shorter tiles re-read them more
+        // often and measured slower even with twice the workgroups)
+        const int cols = sw ? 128 : 256;
+        a.n_chunks = (N0 + cols - 1) / cols;
+        const int m32 = 4;
+        a.tiles_m = (M + 32 * m32 - 1) / (32 * m32);
+        a.n_logical = (long)a.tiles_m * a.n_chunks;
+        a.per_xcd = moe::per_xcd(a.n_logical);
+        const dim3 grid(8 * a.per_xcd), block(256);
+        if (m32 == 4) {
+            if (sw) hipLaunchKernelGGL((k_dense32<4, EPI_SWIGLU>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_dense32<4, EPI_LINEAR>), grid, block, 0, st, a);
+        } else {
+            if (sw) hipLaunchKernelGGL((k_dense32<2, EPI_SWIGLU>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_dense32<2, EPI_LINEAR>), grid, block, 0, st, a);
+        }
         return moe::launch_status(what);
     }
     if (sw) launch_dense_mb_cb<EPI_SWIGLU, false>(p, a, st);

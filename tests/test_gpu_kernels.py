@@ -337,6 +337,8 @@ def test_act_f16p_layout(m, rows, K, seed):
 @pytest.mark.parametrize("M,N,K,with_add,seed", [
     (1, 64, 128, False, 0), (64, 2048, 7168, False, 1), (40, 192, 512, True, 2), (200, 256, 384, True, 3),
     (700, 512, 256, False, 4),
+    (300, 320, 384, True, 5),       # 32x32 tiles: ragged rows and a part-filled column chunk
+    (4100, 4096, 128, True, 6),     # 32x32 tiles, many row tiles, ragged rows
 ])
 def test_linear_bf16(m, M, N, K, with_add, seed):
     say(f"linear M={M} N={N} K={K}")
@@ -353,7 +355,9 @@ def test_linear_bf16(m, M, N, K, with_add, seed):
     assert_bf16_close(np_bf16(y), ref, "linear")
 
 
-@pytest.mark.parametrize("M,H,I,seed", [(64, 256, 128, 0), (64, 7168, 2048, 1), (130, 512, 192, 2)])
+@pytest.mark.parametrize("M,H,I,seed", [(64, 256, 128, 0), (64, 7168, 2048, 1), (130, 512, 192, 2),
+                                        (300, 256, 192, 3),     # 32x32 tiles, ragged rows and columns
+                                        (4096, 128, 2048, 4)])  # 32x32 tiles, many row tiles
 def test_dense_swiglu_and_silu_mul(m, M, H, I, seed):
     say(f"dense swiglu M={M} H={H} I={I}")
     g = np.random.default_rng(seed)
