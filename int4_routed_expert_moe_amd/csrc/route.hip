@@ -34,8 +34,10 @@ __device__ __forceinline__ void tile_load(TileLoad& tl, const uint16_t* __restri
     const int tid = threadIdx.x;
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        const int p = it * 256 + tid;  // 512 pieces of 8 elements
-        const int row = p >> 3, piece = p & 7;
+        // 512 pieces of 8 elements; consecutive lanes take consecutive rows of one
+        // piece, so the transposed LDS stores below hit 64 distinct banks
+        const int p = it * 256 + tid;
+        const int row = p & 63, piece = p >> 6;
         const bool ok = row0 + row < limit;
         tl.v[it] = *reinterpret_cast<const u32x4_t*>(m + (size_t)(ok ? row0 + row : 0) * H + col0 + piece * 8);
         if (!ok) tl.v[it] = u32x4_t{0u, 0u, 0u, 0u};
@@ -46,12 +48,73 @@ __device__ __forceinline__ void tile_store(const TileLoad& tl, float (*dst)[64 +
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int p = it * 256 + tid;
-        const int row = p >> 3, piece = p & 7;
+        const int row = p & 63, piece = p >> 6;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             dst[piece * 8 + 2 * j][row] = __uint_as_float(tl.v[it][j] << 16);
             dst[piece * 8 + 2 * j + 1][row] = __uint_as_float(tl.v[it][j] & 0xFFFF0000u);
         }
+    }
+}
+
+// Stage R = 16*CE rows x 64 hidden elements of the router matrix as fp32,
+// transposed to [i][slot], where row r sits in slot 4*(r / CE) + r % CE (so a
+// thread's CE rows are one 16-byte LDS read); rows at or past `limit` are zero.
+template <int CE>
+struct WTileLoad {
+    static constexpr int R = 16 * CE;
+    static constexpr int IT = (R * 8 + 255) / 256;  // 16-byte pieces per thread
+    u32x4_t v[IT];
+};
+template <int CE>
+__device__ __forceinline__ void wtile_load(WTileLoad<CE>& tl, const uint16_t* __restrict__ m, int row0, int limit,
+                                           int H, int col0) {
+    constexpr int R = WTileLoad<CE>::R;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < WTileLoad<CE>::IT; ++it) {
+        const int p = it * 256 + tid;
+        const int row = p % R, piece = p / R;  // consecutive lanes: consecutive rows of one piece
+        const bool ok = p < R * 8 && row0 + row < limit;
+        tl.v[it] = *reinterpret_cast<const u32x4_t*>(m + (size_t)(ok ? row0 + row : 0) * H + col0 + piece * 8);
+        if (!ok) tl.v[it] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+}
+template <int CE>
+__device__ __forceinline__ void wtile_store(const WTileLoad<CE>& tl, float (*dst)[64 + 4]) {
+    constexpr int R = WTileLoad<CE>::R;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < WTileLoad<CE>::IT; ++it) {
+        const int p = it * 256 + tid;
+        if (p >= R * 8) continue;
+        const int row = p % R, piece = p / R;
+        const int slot = 4 * (row / CE) + row % CE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            dst[piece * 8 + 2 * j][slot] = __uint_as_float(tl.v[it][j] << 16);
+            dst[piece * 8 + 2 * j + 1][slot] = __uint_as_float(tl.v[it][j] & 0xFFFF0000u);
+        }
+    }
+}
+
+// One 64-long ascending chain per (token, expert) of a 4 x CE register tile
+// (experts in the slot layout of wtile_store).
+template <int CE>
+__device__ __forceinline__ void block_chain_ce(const float (*xs)[64 + 4], const float (*ws)[64 + 4], int tt, int te,
+                                               float (&acc)[4][CE]) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < CE; ++c) acc[a][c] = 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < kRouteKC; ++i) {
+        const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[i][4 * tt]);
+        const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(&ws[i][4 * te]);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < CE; ++c) acc[a][c] = __builtin_fmaf(xv[a], wv[c], acc[a][c]);
     }
 }
 
@@ -79,49 +142,52 @@ __device__ __forceinline__ void block_chain(const float (*xs)[64 + 4], const flo
 // tiles are staged in LDS as fp32, double buffered: the next block's loads are
 // in flight during the current block's chains (one LDS-only barrier per block).
 // Grid: (ceil(E/64), ceil(T/64)).
+template <int CE>
 __global__ __launch_bounds__(256) void k_router_full(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                      int T, int H, int E, float* __restrict__ logits) {
+    constexpr int R = 16 * CE;  // experts per block
     __shared__ __attribute__((aligned(16))) float xs[2][kRouteKC][64 + 4];  // [i][t]
-    __shared__ __attribute__((aligned(16))) float ws[2][kRouteKC][64 + 4];  // [i][e]
+    __shared__ __attribute__((aligned(16))) float ws[2][kRouteKC][64 + 4];  // [i][slot]
     const int tid = threadIdx.x;
-    const int e0 = blockIdx.x * 64;
+    const int e0 = blockIdx.x * R;
     const int t0 = blockIdx.y * kRouteTok;
     const int NB = H / kRouteKC;
     const int tt = tid >> 4, te = tid & 15;
-    TileLoad lx, lw;
+    TileLoad lx;
+    WTileLoad<CE> lw;
     tile_load(lx, x, t0, T, H, 0);
-    tile_load(lw, w, e0, E, H, 0);
+    wtile_load<CE>(lw, w, e0, E, H, 0);
     tile_store(lx, xs[0]);
-    tile_store(lw, ws[0]);
+    wtile_store<CE>(lw, ws[0]);
     lds_barrier();
-    float total[4][4];
+    float total[4][CE];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) total[a][c] = 0.0f;
+        for (int c = 0; c < CE; ++c) total[a][c] = 0.0f;
     for (int b = 0; b < NB; ++b) {
         const int buf = b & 1;
         const int bn = min(b + 1, NB - 1);  // past the end: a redundant in-bounds load, never used
         tile_load(lx, x, t0, T, H, bn * kRouteKC);
-        tile_load(lw, w, e0, E, H, bn * kRouteKC);
-        float acc[4][4];
-        block_chain(xs[buf], ws[buf], tt, te, acc);
+        wtile_load<CE>(lw, w, e0, E, H, bn * kRouteKC);
+        float acc[4][CE];
+        block_chain_ce<CE>(xs[buf], ws[buf], tt, te, acc);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) total[a][c] = total[a][c] + acc[a][c];  // block sums in ascending order
+            for (int c = 0; c < CE; ++c) total[a][c] = total[a][c] + acc[a][c];  // block sums in ascending order
         tile_store(lx, xs[buf ^ 1]);
-        tile_store(lw, ws[buf ^ 1]);
+        wtile_store<CE>(lw, ws[buf ^ 1]);
         lds_barrier();
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int t = t0 + 4 * tt + a;
         if (t >= T) continue;
-        float* dst = logits + (size_t)t * E + e0 + 4 * te;
+        float* dst = logits + (size_t)t * E + e0 + CE * te;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            if (e0 + 4 * te + c < E) dst[c] = total[a][c];
+        for (int c = 0; c < CE; ++c)
+            if (e0 + CE * te + c < E) dst[c] = total[a][c];
     }
 }
 
@@ -308,7 +374,14 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const floa
         const long n = (long)T * E;
         hipLaunchKernelGGL(k_router_blocksum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, T, NB, E, logits);
     } else {
-        hipLaunchKernelGGL(k_router_full, dim3((E + 63) / 64, tb), dim3(256), 0, st, x, w_router, T, H, E, logits);
+        // 64 or 48 experts per block, whichever fills the CUs more evenly (48:
+        // 8 blocks per 64 tokens at 384 experts)
+        auto fill = [](long n) { return (double)n / (double)(256 * ((n + 255) / 256)); };
+        const long n64 = (long)((E + 63) / 64) * tb, n48 = (long)((E + 47) / 48) * tb;
+        if (fill(n48) > fill(n64))
+            hipLaunchKernelGGL(k_router_full<3>, dim3((E + 47) / 48, tb), dim3(256), 0, st, x, w_router, T, H, E, logits);
+        else
+            hipLaunchKernelGGL(k_router_full<4>, dim3((E + 63) / 64, tb), dim3(256), 0, st, x, w_router, T, H, E, logits);
     }
     int rc = launch_status("moe_route logits");
     if (rc) return rc;

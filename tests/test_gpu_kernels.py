@@ -51,6 +51,8 @@ def _scales(g, shape):
 @pytest.mark.parametrize("T,H,E,k,seed", [
     (1, 128, 16, 1, 0), (37, 256, 16, 2, 1), (64, 7168, 384, 8, 2), (300, 1024, 384, 8, 3),
     (130, 512, 1000, 16, 4), (64, 256, 8, 8, 5),
+    (300, 512, 100, 4, 6),      # large-batch path, 48-expert blocks, ragged last block
+    (8192, 128, 384, 8, 7),     # large-batch path, 64-expert blocks
 ])
 def test_route_bitexact(m, T, H, E, k, seed):
     say(f"route T={T} H={H} E={E} k={k}")
