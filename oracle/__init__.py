@@ -203,6 +203,28 @@ def topk_from_scores(scores, bias, k, renormalize=True):
     return idx, w
 
 
+def topk_grouped_from_scores(scores, bias, k, n_group, topk_group, renormalize=True, scale=1.0):
+    """Group-limited selection (see oracle_topk_grouped_from_scores)."""
+    scores = _c(scores, np.float32)
+    bias = _c(bias, np.float32)
+    T, E = scores.shape
+    if (n_group < 1 or E % n_group or not 1 <= topk_group <= n_group or k > topk_group * (E // n_group)
+            or (n_group > 1 and E // n_group < 2)):
+        raise ValueError("bad group configuration")
+    idx = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float32)
+    lib().oracle_topk_grouped_from_scores(_p(scores), _p(bias), T, E, k, n_group, topk_group,
+                                          int(bool(renormalize)), ctypes.c_float(scale), _p(idx), _p(w))
+    return idx, w
+
+
+def route_grouped(x, wr, bias, k, n_group, topk_group, renormalize=True, scale=1.0):
+    """Routing with group-limited selection: logits and sigmoid as route(), then
+    topk_grouped_from_scores."""
+    _, _, _, scores = route(x, wr, bias, k, renormalize, return_scores=True)
+    return topk_grouped_from_scores(scores, bias, k, n_group, topk_group, renormalize, scale)
+
+
 def route(x, wr, bias, k, renormalize=True, return_scores=False):
     """Returns (topk_idx [T,k] int32, topk_w [T,k] f32[, logits, scores])."""
     x = _c(x, np.uint16)

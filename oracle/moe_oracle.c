@@ -215,6 +215,70 @@ void oracle_topk_from_scores(const float* scores, const float* bias, int T, int 
     }
 }
 
+/* Group-limited selection ("Kimi K2.5 donor reference", MoEGate.forward
+ * records: group scores, group idx, score mask, topk idx, denominator; the
+ * records name these statements without their code).  Readings taken:
+ *   - the E experts form n_group groups of E/n_group consecutive indices;
+ *   - a group's score is the sum of its two largest biased scores c = s + b
+ *     (largest + second largest, one fp32 add);
+ *   - the topk_group groups with the largest scores are kept, ties to the
+ *     lower group index;
+ *   - experts outside the kept groups cannot be selected; the top k of c is
+ *     taken among the rest, ties to the lower expert index;
+ *   - weights: as oracle_topk_from_scores, then each multiplied by the routed
+ *     scaling factor (fp32): w = (s / d) * scale.
+ * n_group = 1 (or topk_group = n_group) is the ungrouped selection. */
+void oracle_topk_grouped_from_scores(const float* scores, const float* bias, int T, int E, int k, int n_group,
+                                     int topk_group, int renormalize, float scale, int32_t* topk_idx,
+                                     float* topk_w) {
+    const int G = E / n_group;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const float* s = scores + (size_t)t * E;
+        float* c = (float*)malloc(sizeof(float) * (size_t)E);
+        float* gs = (float*)malloc(sizeof(float) * (size_t)n_group);
+        char* keep = (char*)calloc((size_t)n_group, 1);
+        char* taken = (char*)calloc((size_t)E, 1);
+        for (int e = 0; e < E; ++e) c[e] = s[e] + bias[e];
+        for (int g = 0; g < n_group; ++g) {
+            int b1 = -1, b2 = -1;
+            for (int e = g * G; e < (g + 1) * G; ++e) {
+                if (b1 < 0 || c[e] > c[b1]) { b2 = b1; b1 = e; }
+                else if (b2 < 0 || c[e] > c[b2]) b2 = e;
+            }
+            gs[g] = (G >= 2) ? c[b1] + c[b2] : c[b1];
+        }
+        for (int j = 0; j < topk_group; ++j) {
+            int best = -1;
+            for (int g = 0; g < n_group; ++g) {
+                if (keep[g]) continue;
+                if (best < 0 || gs[g] > gs[best]) best = g;
+            }
+            keep[best] = 1;
+        }
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e] || !keep[e / G]) continue;
+                if (best < 0 || c[e] > c[best]) best = e;
+            }
+            taken[best] = 1;
+            topk_idx[(size_t)t * k + j] = best;
+        }
+        float d = 0.0f;
+        for (int j = 0; j < k; ++j) d = d + s[topk_idx[(size_t)t * k + j]];
+        d = d + 1e-20f;
+        for (int j = 0; j < k; ++j) {
+            const float v = s[topk_idx[(size_t)t * k + j]];
+            topk_w[(size_t)t * k + j] = (renormalize ? v / d : v) * scale;
+        }
+        free(c);
+        free(gs);
+        free(keep);
+        free(taken);
+    }
+}
+
 void oracle_route(const uint16_t* x, const uint16_t* wr, const float* bias, int T, int H, int E,
                   int k, int renormalize, int32_t* topk_idx, float* topk_w,
                   float* logits_out /* [T,E] or NULL */, float* scores_out /* [T,E] or NULL */) {

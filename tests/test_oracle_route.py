@@ -176,3 +176,76 @@ def test_zipf_fixture_routing_on_exact_workload():
     assert counts[dead].sum() == 0
     assert counts.sum() == cfg["T"] * cfg["k"]
     assert counts.max() > cfg["T"] // 2
+
+
+# ---------------------------------------------------------------- group-limited selection
+# ("Kimi K2.5 donor reference", MoEGate.forward records: group scores, group idx,
+# score mask, topk idx; readings in oracle_topk_grouped_from_scores)
+
+def _scores(g, T, E):
+    s = g.uniform(0.01, 0.99, (T, E)).astype(np.float32)
+    b = g.uniform(-0.1, 0.1, E).astype(np.float32)
+    return s, b
+
+
+@pytest.mark.parametrize("E,n_group,k", [(16, 4, 3), (384, 8, 8)])
+def test_grouped_with_every_group_kept_is_plain_routing(E, n_group, k):
+    g = np.random.default_rng(11)
+    s, b = _scores(g, 40, E)
+    idx0, w0 = oracle.topk_from_scores(s, b, k)
+    for ng, tg in ((1, 1), (n_group, n_group)):
+        idx, w = oracle.topk_grouped_from_scores(s, b, k, ng, tg)
+        np.testing.assert_array_equal(idx, idx0)
+        np.testing.assert_array_equal(w, w0)
+
+
+@pytest.mark.parametrize("E,n_group,topk_group,k,seed", [(64, 8, 3, 6, 0), (384, 8, 4, 8, 1), (48, 4, 1, 5, 2)])
+def test_grouped_selection_is_sort_of_masked_scores(E, n_group, topk_group, k, seed):
+    """Group scores from a library sort of each group (two largest, added in fp32),
+    kept groups and experts from stable sorts with the index as tie-breaker."""
+    g = np.random.default_rng(seed)
+    T = 50
+    s, b = _scores(g, T, E)
+    idx, _ = oracle.topk_grouped_from_scores(s, b, k, n_group, topk_group)
+    c = (s + b).astype(np.float32)
+    G = E // n_group
+    top2 = np.sort(c.reshape(T, n_group, G), axis=2)[:, :, ::-1][:, :, :2]
+    gs = (top2[:, :, 0] + top2[:, :, 1]).astype(np.float32)
+    for t in range(T):
+        keep = np.lexsort((np.arange(n_group), -gs[t]))[:topk_group]
+        allowed = np.isin(np.arange(E) // G, keep)
+        cand = np.nonzero(allowed)[0]
+        order = cand[np.lexsort((cand, -c[t, cand]))][:k]
+        np.testing.assert_array_equal(idx[t], order)
+
+
+def test_grouped_worked_example():
+    """Eight experts in four groups of two.  Biased scores
+    c = [0.9, 0.1 | 0.5, 0.5 | 0.8, 0.0 | 0.3, 0.3] give group scores
+    [1.0, 1.0, 0.8, 0.6]; keeping two groups keeps 0 and 1, so the top two are
+    experts 0 and 2 (2 before its tie 3), where ungrouped routing picks 0 and 4."""
+    c = np.array([[0.9, 0.1, 0.5, 0.5, 0.8, 0.0, 0.3, 0.3]], dtype=np.float32)
+    s = c.copy()
+    b = np.zeros(8, dtype=np.float32)
+    idx, w = oracle.topk_grouped_from_scores(s, b, 2, 4, 2)
+    np.testing.assert_array_equal(idx, [[0, 2]])
+    idx_plain, _ = oracle.topk_from_scores(s, b, 2)
+    np.testing.assert_array_equal(idx_plain, [[0, 4]])
+    d = np.float32(np.float32(0.9) + np.float32(0.5)) + np.float32(1e-20)
+    np.testing.assert_array_equal(w, [[np.float32(0.9) / d, np.float32(0.5) / d]])
+
+
+def test_grouped_tied_groups_keep_lower_index():
+    """Groups 1 and 3 tie on their score; with one group kept, group 1 wins."""
+    c = np.array([[0.1, 0.2, 0.6, 0.3, 0.2, 0.1, 0.3, 0.6]], dtype=np.float32)
+    idx, _ = oracle.topk_grouped_from_scores(c, np.zeros(8, np.float32), 2, 4, 1)
+    np.testing.assert_array_equal(idx, [[2, 3]])
+
+
+def test_grouped_scaling_factor_multiplies_weights():
+    g = np.random.default_rng(5)
+    s, b = _scores(g, 30, 64)
+    _, w1 = oracle.topk_grouped_from_scores(s, b, 6, 8, 3, True, 1.0)
+    _, w25 = oracle.topk_grouped_from_scores(s, b, 6, 8, 3, True, 2.5)
+    np.testing.assert_array_equal(w25, (w1 * np.float32(2.5)).astype(np.float32))
+    assert np.all(np.abs(w1.sum(axis=1) - 1.0) <= 6 * 2.0 ** -24 * 4)
