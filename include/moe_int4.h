@@ -91,6 +91,22 @@ int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, in
               int k, int renormalize, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
               void* stream);
 
+/* Group-limited routing ("Kimi K2.5 donor reference", MoEGate.forward records
+ * "group scores", "group idx", "score mask", "( , topk idx)", "denominator";
+ * the records name those steps without their code, so the reading is stated):
+ * as moe_route, except that the E experts form n_group groups of E/n_group
+ * consecutive indices; a group scores the sum of its two largest biased scores
+ * s + bias (one fp32 add); the topk_group best groups are kept, ties to the
+ * lower group; the k experts are selected among the kept groups only; and
+ * each weight is multiplied by routed_scale (fp32, after the renormalisation).
+ * n_group = 1 (or topk_group = n_group) with routed_scale = 1 is moe_route.
+ * Requires n_group <= 64 dividing E into groups of at least 2 (when n_group >
+ * 1), 1 <= topk_group <= n_group, k <= topk_group * E / n_group, routed_scale
+ * finite.  Same workspace as moe_route.  Bit-exact and deterministic. */
+int moe_route_grouped(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E,
+                      int k, int renormalize, int n_group, int topk_group, float routed_scale,
+                      int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Permutation ("Kimi-K3 latent MoE" page, Code: moe_infer's per-expert counts,
  * argsort of the flattened expert ids and start/end walk; "Kimi K2.5 donor

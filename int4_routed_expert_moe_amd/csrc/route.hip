@@ -258,8 +258,8 @@ __global__ __launch_bounds__(256) void k_router_blocksum(const float* __restrict
 template <int NQ>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E,
-                                                    int k, int renormalize,
-                                                    int32_t* __restrict__ topk_idx,
+                                                    int k, int renormalize, int n_group, int topk_group,
+                                                    float scale, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ topk_w) {
     const int lane = lane_id();
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -279,6 +279,58 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
             s[q] = 0.0f;
             key[q] = -__builtin_huge_valf();
             taken |= 1u << q;
+        }
+    }
+    // Group-limited selection ("Kimi K2.5 donor reference", MoEGate.forward
+    // records: group scores, group idx, score mask): a group of E/n_group
+    // consecutive experts scores the sum of its two largest biased scores; the
+    // topk_group best groups are kept (ties to the lower group); experts of the
+    // other groups are marked taken, so the selection below never picks them.
+    if (n_group > 1) {
+        const int G = E / n_group;
+        float gsc = -__builtin_huge_valf();  // lane g holds group g's score
+        for (int g = 0; g < n_group; ++g) {
+            float m1 = -__builtin_huge_valf(), m2 = -__builtin_huge_valf();
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int e = lane + MOE_WAVE * q;
+                if (e < E && e / G == g) {
+                    if (key[q] > m1) {
+                        m2 = m1;
+                        m1 = key[q];
+                    } else if (key[q] > m2) {
+                        m2 = key[q];
+                    }
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {  // merge two (largest, second) pairs
+                const float o1 = __shfl_xor(m1, off), o2 = __shfl_xor(m2, off);
+                const float n2 = fmaxf(fminf(m1, o1), fmaxf(m2, o2));
+                m1 = fmaxf(m1, o1);
+                m2 = n2;
+            }
+            if (lane == g) gsc = m1 + m2;
+        }
+        uint64_t keep = 0;
+        for (int j = 0; j < topk_group; ++j) {
+            float bv = (lane < n_group && !((keep >> lane) & 1ull)) ? gsc : -__builtin_huge_valf();
+            int bg = (lane < n_group && !((keep >> lane) & 1ull)) ? lane : 0x7FFFFFFF;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int og = __shfl_xor(bg, off);
+                if (og != 0x7FFFFFFF && (bg == 0x7FFFFFFF || ov > bv || (ov == bv && og < bg))) {
+                    bv = ov;
+                    bg = og;
+                }
+            }
+            keep |= 1ull << bg;
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int e = lane + MOE_WAVE * q;
+            if (e < E && !((keep >> (e / G)) & 1ull)) taken |= 1u << q;
         }
     }
     int sel_e = 0;
@@ -316,15 +368,15 @@ __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ lo
     denom = denom + 1e-20f;
     if (lane < k) {
         topk_idx[(size_t)t * k + lane] = sel_e;
-        topk_w[(size_t)t * k + lane] = renormalize ? sel_s / denom : sel_s;
+        topk_w[(size_t)t * k + lane] = (renormalize ? sel_s / denom : sel_s) * scale;  // routed scaling factor
     }
 }
 
 template <int NQ>
-void launch_topk(const float* logits, const float* bias, int T, int E, int k, int renorm,
-                 int32_t* idx, float* w, hipStream_t st) {
+void launch_topk(const float* logits, const float* bias, int T, int E, int k, int renorm, int n_group,
+                 int topk_group, float scale, int32_t* idx, float* w, hipStream_t st) {
     hipLaunchKernelGGL(k_route_topk<NQ>, dim3((T + 3) / 4), dim3(256), 0, st, logits, bias, T, E,
-                       k, renorm, idx, w);
+                       k, renorm, n_group, topk_group, scale, idx, w);
 }
 
 // Few tokens: all (token, expert, block) sums in parallel, summed in the top-k
@@ -343,9 +395,10 @@ extern "C" size_t moe_route_workspace_bytes(int T, int H, int E) {
     return (size_t)T * (size_t)E * sizeof(float);
 }
 
-extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
-                         int H, int E, int k, int renormalize, int32_t* topk_idx, float* topk_w,
-                         void* ws, size_t ws_bytes, void* stream) {
+namespace {
+int route_impl(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H, int E, int k,
+               int renormalize, int n_group, int topk_group, float scale, int32_t* topk_idx, float* topk_w,
+               void* ws, size_t ws_bytes, void* stream) {
     using namespace moe;
     if (T < 0 || H <= 0 || E <= 0 || k <= 0)
         return fail(MOE_ERR_INVALID_ARG, "moe_route: bad sizes T=%d H=%d E=%d k=%d", T, H, E, k);
@@ -386,10 +439,36 @@ extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const floa
     int rc = launch_status("moe_route logits");
     if (rc) return rc;
     const int nq = (E + MOE_WAVE - 1) / MOE_WAVE;
-    if (nq <= 1) launch_topk<1>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 2) launch_topk<2>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 4) launch_topk<4>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else if (nq <= 8) launch_topk<8>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
-    else launch_topk<16>(logits, bias, T, E, k, renormalize, topk_idx, topk_w, st);
+    if (nq <= 1) launch_topk<1>(logits, bias, T, E, k, renormalize, n_group, topk_group, scale, topk_idx, topk_w, st);
+    else if (nq <= 2) launch_topk<2>(logits, bias, T, E, k, renormalize, n_group, topk_group, scale, topk_idx, topk_w, st);
+    else if (nq <= 4) launch_topk<4>(logits, bias, T, E, k, renormalize, n_group, topk_group, scale, topk_idx, topk_w, st);
+    else if (nq <= 8) launch_topk<8>(logits, bias, T, E, k, renormalize, n_group, topk_group, scale, topk_idx, topk_w, st);
+    else launch_topk<16>(logits, bias, T, E, k, renormalize, n_group, topk_group, scale, topk_idx, topk_w, st);
     return launch_status("moe_route topk");
+}
+}  // namespace
+
+extern "C" int moe_route(const uint16_t* x, const uint16_t* w_router, const float* bias, int T,
+                         int H, int E, int k, int renormalize, int32_t* topk_idx, float* topk_w,
+                         void* ws, size_t ws_bytes, void* stream) {
+    return route_impl(x, w_router, bias, T, H, E, k, renormalize, 1, 1, 1.0f, topk_idx, topk_w, ws, ws_bytes,
+                      stream);
+}
+
+extern "C" int moe_route_grouped(const uint16_t* x, const uint16_t* w_router, const float* bias, int T, int H,
+                                 int E, int k, int renormalize, int n_group, int topk_group, float routed_scale,
+                                 int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+    using namespace moe;
+    if (n_group < 1 || topk_group < 1 || topk_group > n_group)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route_grouped: n_group=%d topk_group=%d", n_group, topk_group);
+    if (!(routed_scale == routed_scale) || routed_scale == __builtin_huge_valf() ||
+        routed_scale == -__builtin_huge_valf())
+        return fail(MOE_ERR_INVALID_ARG, "moe_route_grouped: routed_scale must be finite");
+    if (E > 0 && (n_group > 64 || E % n_group != 0 || (n_group > 1 && E / n_group < 2) ||
+                  k > topk_group * (E / n_group)))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_route_grouped: need n_group <= 64 dividing E into groups of 2+ and k <= topk_group*E/n_group "
+                    "(E=%d n_group=%d topk_group=%d k=%d)", E, n_group, topk_group, k);
+    return route_impl(x, w_router, bias, T, H, E, k, renormalize, n_group, topk_group, routed_scale, topk_idx,
+                      topk_w, ws, ws_bytes, stream);
 }

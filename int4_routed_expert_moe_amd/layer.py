@@ -59,6 +59,10 @@ class MoELayer:
         self.latent = latent
         self.E, self.k, self.H, self.I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
         self.Kin = cfg.get("L") or cfg["H"]  # width the routed experts see
+        # group-limited routing (1 group, scale 1: plain sigmoid top-k)
+        self.n_group = int(cfg.get("n_group", 1))
+        self.topk_group = int(cfg.get("topk_group", 1))
+        self.routed_scale = float(cfg.get("routed_scale", 1.0))
         self._ws = {}
         self._side = None
         self.device = router_w.device
@@ -170,7 +174,11 @@ class MoELayer:
         mark("start")
         E, k, H, I, Kin = self.E, self.k, self.H, self.I, self.Kin
         ex = self.ex
-        _m.moe_route(x, self.router_w, self.router_b, k, True, w["topk_idx"], w["topk_w"], w["route_ws"])
+        if self.n_group == 1 and self.routed_scale == 1.0:
+            _m.moe_route(x, self.router_w, self.router_b, k, True, w["topk_idx"], w["topk_w"], w["route_ws"])
+        else:
+            _m.moe_route_grouped(x, self.router_w, self.router_b, k, True, self.n_group, self.topk_group,
+                                 self.routed_scale, w["topk_idx"], w["topk_w"], w["route_ws"])
         mark("moe_route")
         _m.moe_permute(w["topk_idx"], E, w["counts"], w["offsets"], w["sorted_slot"], w["slot_pos"])
         mark("moe_permute")

@@ -41,6 +41,7 @@ EXPORTS = {
     "moe_last_error_detail": ([], ctypes.c_char_p),
     "moe_route_workspace_bytes": ([_I, _I, _I], _SZ),
     "moe_route": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
+    "moe_route_grouped": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _SZ, _P], _I),
     "moe_permute": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "moe_quant_act_int8": ([_P, _I, _I, _P, _P, _P], _I),
     "moe_int4_prepack": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
@@ -114,6 +115,19 @@ def moe_route(x, w_router, bias, k, renormalize, topk_idx, topk_w, ws):
     _check("moe_route", _lib.moe_route(_ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, int(bool(renormalize)),
                                        _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream()))
+
+
+def moe_route_grouped(x, w_router, bias, k, renormalize, n_group, topk_group, routed_scale, topk_idx, topk_w, ws):
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(w_router, torch.bfloat16, (E, H), "w_router")
+    _need(bias, torch.float32, (E,), "bias")
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _check("moe_route_grouped", _lib.moe_route_grouped(
+        _ptr(x), _ptr(w_router), _ptr(bias), T, H, E, k, int(bool(renormalize)), n_group, topk_group,
+        float(routed_scale), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel() * ws.element_size(), _stream()))
 
 
 def moe_permute(topk_idx, E, counts, offsets, sorted_slot, slot_pos):

@@ -414,7 +414,11 @@ def layer_tokens(inp, tokens, topk_idx=None, topk_w=None, want_intermediates=Fal
     tokens = np.asarray(tokens, dtype=np.int64)
     x = inp["x"][tokens]
     if topk_idx is None:
-        idx, w = route(x, inp["router_w"], inp["router_b"], k, True)
+        if cfg.get("n_group", 1) != 1 or cfg.get("routed_scale", 1.0) != 1.0:
+            idx, w = route_grouped(x, inp["router_w"], inp["router_b"], k, int(cfg.get("n_group", 1)),
+                                   int(cfg.get("topk_group", 1)), True, float(cfg.get("routed_scale", 1.0)))
+        else:
+            idx, w = route(x, inp["router_w"], inp["router_b"], k, True)
     else:
         idx, w = topk_idx[tokens], topk_w[tokens]
     n = len(tokens)

@@ -107,6 +107,16 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert _status(lib, pp, fake, fake, 2, 32, 256, fake, P(0x200000), null) == -1
     assert _status(lib, pp, fake, P(0x3004), 2, 32, 256, P(0x100000), P(0x200000), null) == -1
     assert _status(lib, pp, null, null, 0, 32, 256, null, null, null) == 0
+    # grouped routing: topk_group > n_group, groups not dividing E, k beyond the kept groups, NaN scale
+    rg = "moe_route_grouped"
+    lib.moe_route_grouped.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+    big = ctypes.c_size_t(1 << 30)
+    assert _status(lib, rg, fake, fake, fake, 4, 256, 64, 4, 1, 4, 5, 1.0, fake, fake, fake, big, null) == -1
+    assert _status(lib, rg, fake, fake, fake, 4, 256, 64, 4, 1, 5, 2, 1.0, fake, fake, fake, big, null) == -2
+    assert _status(lib, rg, fake, fake, fake, 4, 256, 64, 9, 1, 8, 1, 1.0, fake, fake, fake, big, null) == -2
+    assert _status(lib, rg, fake, fake, fake, 4, 256, 64, 4, 1, 8, 2, float("nan"), fake, fake, fake, big, null) == -1
+    assert _status(lib, rg, null, null, null, 0, 256, 64, 4, 1, 8, 2, 1.0, null, null, null, ctypes.c_size_t(0), null) == 0
     # staging conversion: K not a multiple of 8, null pointer, overlap, zero rows
     assert _status(lib, "moe_act_f16p", fake, 4, 12, P(0x200000), null) == -2
     assert _status(lib, "moe_act_f16p", null, 4, 16, P(0x200000), null) == -1

@@ -81,6 +81,34 @@ def test_route_bitexact(m, T, H, E, k, seed):
     np.testing.assert_array_equal(wt.cpu().numpy(), rw2)
 
 
+@pytest.mark.parametrize("T,H,E,k,n_group,topk_group,scale,seed", [
+    (64, 7168, 384, 8, 8, 4, 2.5, 0),   # decode shape, small-batch logits path
+    (300, 512, 384, 8, 8, 4, 1.0, 1),   # large-batch path
+    (37, 256, 64, 6, 4, 2, 1.0, 2),
+    (50, 256, 96, 4, 48, 3, 0.75, 3),   # groups of two experts
+    (40, 256, 64, 5, 1, 1, 1.0, 4),     # one group: plain routing
+])
+def test_route_grouped_bitexact(m, T, H, E, k, n_group, topk_group, scale, seed):
+    say(f"route grouped T={T} H={H} E={E} k={k} groups {topk_group}/{n_group}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (T, H))
+    w = _rand_bf16(g, (E, H), 0.02)
+    b = g.uniform(-0.1, 0.1, E).astype(np.float32)
+    # exact ties: duplicated router rows with equal bias, across two groups
+    w[E // 2 + 1] = w[1]
+    b[E // 2 + 1] = b[1]
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.moe_route_workspace_bytes(T, H, E), dtype=torch.uint8, device="cuda")
+    for renorm in (True, False):
+        ridx, rw = oracle.route_grouped(x, w, b, k, n_group, topk_group, renorm, scale)
+        m.moe_route_grouped(bf16_dev(x), bf16_dev(w), torch.from_numpy(b).cuda(), k, renorm, n_group, topk_group,
+                            scale, idx, wt, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+        np.testing.assert_array_equal(wt.cpu().numpy(), rw)
+
+
 def test_sigmoid_matches_oracle_on_a_sweep(m):
     """Route with one expert row per logit value: the selected weight (renormalise
     off, k=E) is the sigmoid of that logit, bit for bit."""

@@ -113,3 +113,26 @@ def test_layer_edge_token_counts():
     # empty input is a no-op
     out = L.forward(bf16_dev(inp["x"][:0]))
     assert out.shape[0] == 0
+
+
+def test_layer_group_limited_routing():
+    """The tiny workload with group-limited routing (4 groups of 4 experts, 2 kept,
+    routed scaling factor 1.5): routing bit-exact, outputs within the bf16 bar."""
+    from int4_routed_expert_moe_amd.layer import MoELayer
+    base = inputs(1)
+    inp = dict(base)
+    inp["cfg"] = dict(base["cfg"], n_group=4, topk_group=2, routed_scale=1.5)
+    cfg = inp["cfg"]
+    L = MoELayer.from_numpy(inp, "cuda")
+    say("layer forward workload 1 with group-limited routing")
+    out = L.forward(bf16_dev(inp["x"]))
+    torch.cuda.synchronize()
+    ws = L.workspace(cfg["T"])
+    ridx, rw = oracle.route_grouped(inp["x"], inp["router_w"], inp["router_b"], cfg["k"], 4, 2, True, 1.5)
+    np.testing.assert_array_equal(ws["topk_idx"].cpu().numpy(), ridx)
+    np.testing.assert_array_equal(ws["topk_w"].cpu().numpy(), rw)
+    plain, _ = oracle.route(inp["x"], inp["router_w"], inp["router_b"], cfg["k"], True)
+    assert (plain != ridx).any()  # the grouping changes some selections on this input
+    ref, inter = oracle.layer_tokens(inp, np.arange(cfg["T"]), want_intermediates=True)
+    terms = (inter["routed"], inter["shared"]) if inp.get("shared") is not None else ()
+    assert_bf16_close(np_bf16(out), ref, "out", addends=terms)
