@@ -85,6 +85,11 @@ def _declare(L):
     L.oracle_exact_linear.argtypes = [P, P, P, P, I32, I32, I32, P]
     L.oracle_experts_exact.argtypes = [P, P, P, I32, I32, I32] + [P] * 6 + [P] * 5
     L.oracle_combine_f32.argtypes = [P, P, I32, I32, I32, P]
+    L.oracle_topk_grouped_from_scores.argtypes = [P, P, I32, I32, I32, I32, I32, I32, F32, P, P]
+    L.oracle_quant_act_int16.argtypes = [P, I32, I32, P, P]
+    L.oracle_group_sums16.argtypes = [P, P, I32, I32, I32, P, P]
+    L.oracle_exact_linear16.argtypes = [P, P, P, P, I32, I32, I32, P]
+    L.oracle_experts_exact16.argtypes = [P, P, P, I32, I32, I32] + [P] * 6 + [P] * 5
     for name in ("oracle_exp_ref_n", "oracle_sigmoid_ref_n", "oracle_silu_ref_n",
                  "oracle_f64_to_bf16_n", "oracle_f32_to_bf16_n"):
         getattr(L, name).argtypes = [P, I32, P]
@@ -93,7 +98,9 @@ def _declare(L):
                "oracle_route", "oracle_permute", "oracle_experts_bf16", "oracle_combine_bf16",
                "oracle_linear_bf16", "oracle_dense_swiglu_bf16", "oracle_rmsnorm_bf16",
                "oracle_quant_f32_int8", "oracle_quant_act_int8", "oracle_group_sums",
-               "oracle_exact_linear", "oracle_experts_exact", "oracle_combine_f32"):
+               "oracle_exact_linear", "oracle_experts_exact", "oracle_combine_f32",
+               "oracle_topk_grouped_from_scores", "oracle_quant_act_int16", "oracle_group_sums16",
+               "oracle_exact_linear16", "oracle_experts_exact16"):
         getattr(L, fn).restype = None
 
 
@@ -214,7 +221,7 @@ def topk_grouped_from_scores(scores, bias, k, n_group, topk_group, renormalize=T
     idx = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float32)
     lib().oracle_topk_grouped_from_scores(_p(scores), _p(bias), T, E, k, n_group, topk_group,
-                                          int(bool(renormalize)), ctypes.c_float(scale), _p(idx), _p(w))
+                                          int(bool(renormalize)), float(scale), _p(idx), _p(w))
     return idx, w
 
 
@@ -379,6 +386,61 @@ def experts_exact(qx, sx, experts, W, want=("y",)):
                                _p(_c(W["wu"], np.uint8)), _p(_c(W["su"], np.uint16)),
                                _p(_c(W["wd"], np.uint8)), _p(_c(W["sd"], np.uint16)),
                                _p(g), _p(u), _p(qh), _p(sh), _p(y))
+    out = {"y": y}
+    for name, v in (("g", g), ("u", u), ("qh", qh), ("sh", sh)):
+        if v is not None:
+            out[name] = v
+    return out
+
+
+# exact mode with 16-bit activations (act_bits = 16)
+
+def quant_act_int16(x):
+    x = _c(x, np.uint16)
+    M, K = x.shape
+    q = np.empty((M, K), dtype=np.int16)
+    s = np.empty((M, K // 32), dtype=np.float32)
+    lib().oracle_quant_act_int16(_p(x), M, K, _p(q), _p(s))
+    return q, s
+
+
+def group_sums16(qx, packed, K, with_int64=False):
+    qx = _c(qx, np.int16)
+    packed = _c(packed, np.uint8)
+    M = qx.shape[0]
+    N = packed.shape[0]
+    G32 = np.empty((M, N, K // 32), dtype=np.int32)
+    G64 = np.empty((M, N, K // 32), dtype=np.int64) if with_int64 else None
+    lib().oracle_group_sums16(_p(qx), _p(packed), M, N, K, _p(G32), _p(G64))
+    return (G32, G64) if with_int64 else G32
+
+
+def exact_linear16(qx, sx, packed, scale):
+    qx = _c(qx, np.int16)
+    sx = _c(sx, np.float32)
+    M, K = qx.shape
+    N = packed.shape[0]
+    y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_exact_linear16(_p(qx), _p(sx), _p(_c(packed, np.uint8)), _p(_c(scale, np.uint16)), M, N, K, _p(y))
+    return y
+
+
+def experts_exact16(qx, sx, experts, W, want=("y",)):
+    qx = _c(qx, np.int16)
+    sx = _c(sx, np.float32)
+    experts = _c(experts, np.int32)
+    P_, H = qx.shape
+    I = W["wg"].shape[1]
+    g = np.empty((P_, I), np.float32) if "g" in want else None
+    u = np.empty((P_, I), np.float32) if "u" in want else None
+    qh = np.empty((P_, I), np.int16) if "qh" in want else None
+    sh = np.empty((P_, I // 32), np.float32) if "sh" in want else None
+    y = np.empty((P_, H), np.float32)
+    lib().oracle_experts_exact16(_p(qx), _p(sx), _p(experts), P_, H, I,
+                                 _p(_c(W["wg"], np.uint8)), _p(_c(W["sg"], np.uint16)),
+                                 _p(_c(W["wu"], np.uint8)), _p(_c(W["su"], np.uint16)),
+                                 _p(_c(W["wd"], np.uint8)), _p(_c(W["sd"], np.uint16)),
+                                 _p(g), _p(u), _p(qh), _p(sh), _p(y))
     out = {"y": y}
     for name, v in (("g", g), ("u", u), ("qh", qh), ("sh", sh)):
         if v is not None:

@@ -611,6 +611,128 @@ void oracle_experts_exact(const int8_t* qx, const float* sx, const int32_t* expe
     }
 }
 
+/* ------------------------------------------------------------------------- */
+/* Exact mode with 16-bit activations (the adaptation's act_bits, whose       */
+/* default the K2.5 source passes as 16).  Readings: the quantiser of the     */
+/* 8-bit mode with 32767 for 127 (scale amax/32767, round-half-even, clamp to */
+/* +-32767, zero group -> scale 0); the int4 x int16 group sums are exact     */
+/* (|G| <= 32 * 8 * 32767 < 2^23); the fold is the 8-bit one,                 */
+/*   acc = fmaf(f32(s_w) * (float)G, s_x, acc),                              */
+/* where the product is now rounded once to fp32 (it is exact for 8 bits).   */
+/* ------------------------------------------------------------------------- */
+
+static void quant_group_f32_i16(const float* v, int n, int16_t* q, float* s) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        for (int i = 0; i < n; ++i) q[i] = 0;
+        *s = 0.0f;
+        return;
+    }
+    float sc = amax / 32767.0f;
+    for (int i = 0; i < n; ++i) {
+        float r = rintf(v[i] / sc);
+        if (r > 32767.0f) r = 32767.0f;
+        if (r < -32767.0f) r = -32767.0f;
+        q[i] = (int16_t)r;
+    }
+    *s = sc;
+}
+
+/* x: [M, K] bf16 -> q [M, K] int16, s [M, K/32] fp32. */
+void oracle_quant_act_int16(const uint16_t* x, int M, int K, int16_t* q, float* s) {
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m) {
+        float v[32];
+        for (int g = 0; g < K / 32; ++g) {
+            for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(x[(size_t)m * K + (size_t)g * 32 + i]);
+            quant_group_f32_i16(v, 32, q + (size_t)m * K + (size_t)g * 32, s + (size_t)m * (K / 32) + g);
+        }
+    }
+}
+
+/* Group sums of int4 weights with int16 activations (int32 and int64). */
+void oracle_group_sums16(const int16_t* qx, const uint8_t* packed, int M, int N, int K, int32_t* G32,
+                         int64_t* G64 /* may be NULL */) {
+    int NG = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            const uint8_t* row = packed + (size_t)n * (K / 2);
+            for (int g = 0; g < NG; ++g) {
+                int32_t a32 = 0;
+                int64_t a64 = 0;
+                for (int i = g * 32; i < g * 32 + 32; ++i) {
+                    int prod = q4_at(row, i) * (int)qx[(size_t)m * K + i];
+                    a32 += prod;
+                    a64 += prod;
+                }
+                G32[((size_t)m * N + n) * NG + g] = a32;
+                if (G64) G64[((size_t)m * N + n) * NG + g] = a64;
+            }
+        }
+}
+
+static float exact_dot16(const int16_t* qx, const float* sx, const uint8_t* wrow, const uint16_t* srow, int K) {
+    float acc = 0.0f;
+    for (int g = 0; g < K / 32; ++g) {
+        int32_t G = 0;
+        for (int i = g * 32; i < g * 32 + 32; ++i) G += q4_at(wrow, i) * (int)qx[i];
+        float cw = bf16_to_f32(srow[g]) * (float)G;
+        acc = fmaf(cw, sx[g], acc);
+    }
+    return acc;
+}
+
+void oracle_exact_linear16(const int16_t* qx, const float* sx, const uint8_t* packed, const uint16_t* scale, int M,
+                           int N, int K, float* y) {
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n)
+            y[(size_t)m * N + n] = exact_dot16(qx + (size_t)m * K, sx + (size_t)m * (K / 32),
+                                               packed + (size_t)n * (K / 2), scale + (size_t)n * (K / 32), K);
+}
+
+/* The expert chain of oracle_experts_exact with 16-bit activations and h. */
+void oracle_experts_exact16(const int16_t* qx, const float* sx, const int32_t* experts, int P, int H, int I,
+                            const uint8_t* wg, const uint16_t* sg, const uint8_t* wu, const uint16_t* su,
+                            const uint8_t* wd, const uint16_t* sd, float* g_out, float* u_out, int16_t* qh_out,
+                            float* sh_out, float* y_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int p = 0; p < P; ++p) {
+        int e = experts[p];
+        const int16_t* xq = qx + (size_t)p * H;
+        const float* xs = sx + (size_t)p * (H / 32);
+        const uint8_t* wge = wg + (size_t)e * I * (H / 2);
+        const uint16_t* sge = sg + (size_t)e * I * (H / 32);
+        const uint8_t* wue = wu + (size_t)e * I * (H / 2);
+        const uint16_t* sue = su + (size_t)e * I * (H / 32);
+        const uint8_t* wde = wd + (size_t)e * H * (I / 2);
+        const uint16_t* sde = sd + (size_t)e * H * (I / 32);
+        float* h = (float*)malloc(sizeof(float) * (size_t)I);
+        int16_t* qh = (int16_t*)malloc(sizeof(int16_t) * (size_t)I);
+        float* sh = (float*)malloc(sizeof(float) * (size_t)(I / 32));
+        for (int n = 0; n < I; ++n) {
+            float g = exact_dot16(xq, xs, wge + (size_t)n * (H / 2), sge + (size_t)n * (H / 32), H);
+            float u = exact_dot16(xq, xs, wue + (size_t)n * (H / 2), sue + (size_t)n * (H / 32), H);
+            if (g_out) g_out[(size_t)p * I + n] = g;
+            if (u_out) u_out[(size_t)p * I + n] = u;
+            h[n] = oracle_silu_ref(g) * u;
+        }
+        for (int gi = 0; gi < I / 32; ++gi) quant_group_f32_i16(h + gi * 32, 32, qh + gi * 32, sh + gi);
+        if (qh_out) memcpy(qh_out + (size_t)p * I, qh, sizeof(int16_t) * (size_t)I);
+        if (sh_out) memcpy(sh_out + (size_t)p * (I / 32), sh, sizeof(float) * (size_t)(I / 32));
+        for (int m = 0; m < H; ++m)
+            y_out[(size_t)p * H + m] = exact_dot16(qh, sh, wde + (size_t)m * (I / 2), sde + (size_t)m * (I / 32), I);
+        free(h);
+        free(qh);
+        free(sh);
+    }
+}
+
 /* Exact-mode combine: out[t][m] = sum_j w[t][j] * y[t][j][m] in fp32, j ascending,
  * each product rounded then added (fp32 output, no bf16 cast). */
 void oracle_combine_f32(const float* y, const float* w, int T, int k, int H, float* out) {

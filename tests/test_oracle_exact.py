@@ -132,3 +132,105 @@ def test_combine_f32():
     exact = np.einsum("tk,tkh->th", w.astype(np.float64), y.astype(np.float64))
     bound = 8 * 2.0 ** -23 * np.einsum("tk,tkh->th", np.abs(w).astype(np.float64), np.abs(y).astype(np.float64))
     assert np.all(np.abs(out - exact) <= bound)
+
+
+# ---------------------------------------------------------------- 16-bit activations (act_bits = 16)
+
+def test_quantiser16_constructed_groups():
+    # amax 2^14 -> s = fl(2^14 / 32767); the amax element maps to 32767, its negative to -32767
+    v = np.zeros(32, np.float32)
+    v[:4] = [16384.0, -16384.0, 1.0, 0.0]
+    q, s = oracle.quant_act_int16(_bf16(v)[None, :])
+    assert s[0, 0] == np.float32(16384.0) / np.float32(32767.0)
+    assert q[0, 0] == 32767 and q[0, 1] == -32767 and q[0, 3] == 0
+    assert q[0, 2] == int(np.rint(np.float32(1.0) / s[0, 0]))
+    q, s = oracle.quant_act_int16(np.zeros((1, 64), np.uint16))
+    assert np.all(s == 0) and np.all(q == 0)
+
+
+def test_quantiser16_properties_random():
+    g = np.random.default_rng(10)
+    x = _bf16(g.standard_normal((40, 256)) * 10.0 ** g.integers(-3, 3, (40, 1)))
+    q, s = oracle.quant_act_int16(x)
+    xf = refmath.bf16_to_f32(x).reshape(40, 8, 32).astype(np.float64)
+    amax = np.abs(xf).max(axis=2)
+    np.testing.assert_allclose(s, amax / 32767.0, rtol=2 ** -23)
+    qg = q.reshape(40, 8, 32).astype(np.float64)
+    assert np.all(np.abs(qg).max(axis=2) == 32767) and q.min() >= -32767
+    err = np.abs(xf - qg * s[..., None].astype(np.float64))
+    assert np.all(err <= s[..., None] * (0.5 + 32768 * 2.0 ** -24))
+
+
+def test_group_sums16_exact_and_bounded():
+    g = np.random.default_rng(11)
+    M, N, K = 5, 9, 256
+    qx = g.integers(-32767, 32768, (M, K)).astype(np.int16)
+    packed = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    G32, G64 = oracle.group_sums16(qx, packed, K, with_int64=True)
+    qw = refmath.unpack_int4_np(packed, K).astype(np.int64)
+    ref = np.einsum("mgi,ngi->mng", qx.astype(np.int64).reshape(M, K // 32, 32), qw.reshape(N, K // 32, 32))
+    np.testing.assert_array_equal(G64, ref)
+    np.testing.assert_array_equal(G32.astype(np.int64), ref)
+    qx = np.full((1, 64), 32767, np.int16)
+    packed = np.full((1, 32), 0x88, np.uint8)
+    assert np.all(oracle.group_sums16(qx, packed, 64) == -8 * 32767 * 32)
+
+
+def test_exact_linear16_power_of_two_closed_form():
+    """With power-of-two scales and a total below 2^24 every step is exact."""
+    g = np.random.default_rng(12)
+    M, N, K = 4, 12, 256
+    qx = g.integers(-2000, 2001, (M, K)).astype(np.int16)  # |total| <= 8 * 32 * 8 * 2000 < 2^24
+    packed = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    qw = refmath.unpack_int4_np(packed, K).astype(np.int64)
+    total = qx.astype(np.int64) @ qw.T
+    for a, b in ((-7, -5), (0, 0), (-12, 3)):
+        sw = np.full((N, K // 32), _bf16(2.0 ** a)[()], np.uint16)
+        sx = np.full((M, K // 32), 2.0 ** b, np.float32)
+        y = oracle.exact_linear16(qx, sx, packed, sw)
+        np.testing.assert_array_equal(y.astype(np.float64), total.astype(np.float64) * 2.0 ** (a + b))
+
+
+def test_exact_linear16_general_within_fp64_bound():
+    g = np.random.default_rng(13)
+    M, N, K = 3, 16, 2048
+    qx = g.integers(-32767, 32768, (M, K)).astype(np.int16)
+    sx = (g.uniform(1e-6, 5e-4, (M, K // 32))).astype(np.float32)
+    packed = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    sw = _bf16(g.uniform(0.005, 0.02, (N, K // 32)))
+    y = oracle.exact_linear16(qx, sx, packed, sw).astype(np.float64)
+    G = oracle.group_sums16(qx, packed, K).astype(np.float64)
+    terms = G * refmath.bf16_to_f32(sw)[None].astype(np.float64) * sx[:, None, :].astype(np.float64)
+    exact = terms.sum(axis=2)
+    # each group: the product s_w*G rounded once, then one fma rounding
+    bound = (K // 32 + 1) * 2.0 ** -24 * np.abs(terms).sum(axis=2) * 1.01
+    assert np.all(np.abs(y - exact) <= bound)
+
+
+def test_exact16_expert_chain():
+    g = np.random.default_rng(14)
+    H, I, E = 256, 128, 3
+    qx = g.integers(-2000, 2001, (E, H)).astype(np.int16)
+    sx = np.full((E, H // 32), 2.0 ** -10, np.float32)
+    W = {}
+    for name, (N, K) in (("g", (I, H)), ("u", (I, H)), ("d", (H, I))):
+        W["w" + name] = g.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    W["sg"] = np.full((E, I, H // 32), _bf16(2.0 ** -7)[()], np.uint16)
+    W["su"] = np.full((E, I, H // 32), _bf16(2.0 ** -6)[()], np.uint16)
+    W["sd"] = _bf16(g.uniform(0.005, 0.02, (E, H, I // 32)))
+    r = oracle.experts_exact16(qx, sx, np.arange(E, dtype=np.int32), W, want=("g", "u", "qh", "sh", "y"))
+    for e in range(E):
+        qg = refmath.unpack_int4_np(W["wg"][e], H).astype(np.int64)
+        qu = refmath.unpack_int4_np(W["wu"][e], H).astype(np.int64)
+        np.testing.assert_array_equal(r["g"][e], (qg @ qx[e].astype(np.int64)) * 2.0 ** -17)
+        np.testing.assert_array_equal(r["u"][e], (qu @ qx[e].astype(np.int64)) * 2.0 ** -16)
+        h64 = refmath.silu64(r["g"][e]) * r["u"][e].astype(np.float64)
+        recon = r["qh"][e].astype(np.float64) * np.repeat(r["sh"][e], 32).astype(np.float64)
+        assert np.abs(r["qh"][e]).max() <= 32767
+        assert np.all(np.abs(recon - h64) <= np.repeat(r["sh"][e], 32) * 0.5 + np.abs(h64) * 2 ** -20 + 1e-30)
+        qd = refmath.unpack_int4_np(W["wd"][e], I).astype(np.float64)
+        sd = np.repeat(refmath.bf16_to_f32(W["sd"][e]).astype(np.float64), 32, axis=1)
+        terms = qd * sd * recon[None, :]
+        exact = terms.sum(axis=1)
+        bound = (I // 32 + 1) * 2.0 ** -24 * np.abs(terms).sum(axis=1) * 1.01 + 1e-30
+        assert np.all(np.abs(r["y"][e] - exact) <= bound)
