@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="1 tiny, 2 K2.5 decode (default), 3 K2.5 prefill, 4 exact-mode Zipf, 5 K3 latent")
     ap.add_argument("--kernel-steps", type=int, default=10, help="forwards timed per kernel with events")
+    ap.add_argument("--act-bits", type=int, default=None, choices=[8, 16],
+                    help="exact workload: activation code width (16: the act_bits = 16 variant)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -184,6 +186,12 @@ def main():
         bias = synthetic.load_bias_file(os.path.join(ROOT, "tests", "golden", "zipf_bias_k25.txt"))
     t_gen = time.perf_counter()
     inp = synthetic.make_inputs(args.workload, router_bias=bias)
+    if args.act_bits is not None:
+        if inp["cfg"]["mode"] != "exact":
+            sys.exit("--act-bits applies to the exact workload only")
+        inp["cfg"] = dict(inp["cfg"], act_bits=args.act_bits)
+        if args.act_bits == 16:
+            inp["cfg"]["name"] = inp["cfg"]["name"] + "_act16"
     cfg = inp["cfg"]
     layer = MoELayer.from_numpy(inp, "cuda")
     x = torch.from_numpy(inp["x"].view(np.int16)).cuda().view(torch.bfloat16)
@@ -253,7 +261,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4xf16-mfma" if cfg["mode"] != "exact" else "int4xint8-exact",
+        "dtype": ("int4xf16-mfma" if cfg["mode"] != "exact"
+                  else "int4xint16-exact" if int(cfg.get("act_bits", 8)) == 16 else "int4xint8-exact"),
         "data": "synthetic (seeded; random-init weights of the layer's shapes)",
         "config": {
             "workload": (f"{cfg['name']}: T={T} hidden={cfg['H']} experts={cfg['E']} top-{cfg['k']} "

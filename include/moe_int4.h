@@ -60,7 +60,7 @@ typedef enum {
     MOE_ERR_LAUNCH = -4,      /* the HIP runtime rejected a kernel launch */
 } moe_status;
 
-enum { MOE_MODE_BF16 = 0, MOE_MODE_EXACT_I8 = 1, MOE_MODE_BF16_F16P = 2 };
+enum { MOE_MODE_BF16 = 0, MOE_MODE_EXACT_I8 = 1, MOE_MODE_BF16_F16P = 2, MOE_MODE_EXACT_I16 = 3 };
 
 /* Version of this ABI (incremented on any signature change). */
 int moe_abi_version(void);
@@ -128,6 +128,10 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, i
  * q = clamp(rint(x / s), -127, 127), ties to even; amax == 0 gives s = 0, q = 0.
  * x [M,K] bf16 -> q [M,K] int8, s [M,K/32] fp32.  Bit-exact. */
 int moe_quant_act_int8(const uint16_t* x, int M, int K, int8_t* q, float* s, void* stream);
+/* The same with 16-bit codes (exact mode with act_bits = 16, the adaptation's
+ * default activation width): s = amax / 32767, q = clamp(rint(x / s), +-32767)
+ * -> q [M,K] int16, s [M,K/32] fp32.  Bit-exact. */
+int moe_quant_act_int16(const uint16_t* x, int M, int K, int16_t* q, float* s, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Weight fragment layout for the grouped GEMMs (a layout step of this library,
@@ -173,6 +177,12 @@ int moe_act_f16p(const uint16_t* x, int rows, int K, uint16_t* out, void* stream
  *     G the exact int32 group dot product; h = silu(g) * u (fp32), quantised
  *     per row and group of 32 like moe_quant_act_int8 -> h = q_h [T*k, I]
  *     int8, h_scale = s_h [T*k, I/32] fp32.  Bit-exact.
+ *   mode MOE_MODE_EXACT_I16 (act_bits = 16): as MOE_MODE_EXACT_I8 with int16
+ *     codes: act = q_x [T,H] int16 (moe_quant_act_int16), G the exact int4 x
+ *     int16 group sum (|G| < 2^23), the fold fma(fl32(s_w * G), s_x, acc) with
+ *     the product rounded once to fp32 (exact for 8-bit codes); h quantised
+ *     to int16 codes (amax/32767) -> h = q_h [T*k, I] int16, h_scale fp32.
+ *     Bit-exact.
  *   mode MOE_MODE_BF16_F16P: the arithmetic of MOE_MODE_BF16 with the
  *     activations already in the fp16 staging format of moe_act_f16p:
  *     act = moe_act_f16p(x) [T,H], and h is written in that format (the
@@ -192,6 +202,8 @@ int moe_int4_grouped_swiglu(int mode, const void* act, const float* act_scale,
  *   MOE_MODE_BF16: h [T*k, I] bf16 -> y [T*k, H] bf16 (= bf16 of the fp32 sum).
  *   MOE_MODE_EXACT_I8: h = q_h int8 with h_scale = s_h -> y [T*k, H] fp32,
  *     the fixed-order group combine as above.  Bit-exact.
+ *   MOE_MODE_EXACT_I16: h = q_h int16 with h_scale = s_h -> y [T*k, H] fp32
+ *     (the 16-bit fold above).  Bit-exact.
  *   MOE_MODE_BF16_F16P: h in the fp16 staging format (as written by
  *     moe_int4_grouped_swiglu in that mode) -> y [T*k, H] bf16, bit-identical
  *     to MOE_MODE_BF16 on the bf16 h. 

@@ -144,6 +144,56 @@ extern "C" int moe_combine(int mode, const void* y, const int32_t* slot_pos, con
     return launch_status(what);
 }
 
+// 16-bit activation codes (exact mode with act_bits = 16): one group of 32 per
+// thread, s = amax / 32767, codes clamped to +-32767.
+__global__ __launch_bounds__(256) void k_quant_act16(const uint16_t* __restrict__ x, long groups, int K,
+                                                     int16_t* __restrict__ q, float* __restrict__ s) {
+    const long gidx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gidx >= groups) return;
+    const long row = gidx / (K / 32);
+    const int g = (int)(gidx % (K / 32));
+    const uint16_t* src = x + (size_t)row * K + (size_t)g * 32;
+    float v[32];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const u32x4_t d = *reinterpret_cast<const u32x4_t*>(src + 8 * p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[8 * p + 2 * i] = __uint_as_float(d[i] << 16);
+            v[8 * p + 2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float sc = amax == 0.0f ? 0.0f : amax / 32767.0f;
+    uint32_t packed[16];
+#pragma unroll
+    for (int w = 0; w < 16; ++w)
+        packed[w] = ((uint32_t)moe_quant_i16(v[2 * w], sc) & 0xFFFFu) |
+                    (((uint32_t)moe_quant_i16(v[2 * w + 1], sc) & 0xFFFFu) << 16);
+    int16_t* dst = q + (size_t)row * K + (size_t)g * 32;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        *reinterpret_cast<u32x4_t*>(dst + 8 * p) =
+            u32x4_t{packed[4 * p], packed[4 * p + 1], packed[4 * p + 2], packed[4 * p + 3]};
+    s[gidx] = sc;
+}
+
+extern "C" int moe_quant_act_int16(const uint16_t* x, int M, int K, int16_t* q, float* s, void* stream) {
+    using namespace moe;
+    const char* what = "moe_quant_act_int16";
+    if (M < 0 || K <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes", what);
+    if (K % 32) return fail(MOE_ERR_UNSUPPORTED, "%s: K=%d not a multiple of 32", what, K);
+    if (M == 0) return MOE_OK;
+    if (!x || !q || !s) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    if (!aligned16(x) || !aligned16(q)) return fail(MOE_ERR_INVALID_ARG, "%s: x, q must be 16-byte aligned", what);
+    const long groups = (long)M * (K / 32);
+    hipLaunchKernelGGL(k_quant_act16, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, as_stream(stream), x,
+                       groups, K, q, s);
+    return launch_status(what);
+}
+
 extern "C" int moe_quant_act_int8(const uint16_t* x, int M, int K, int8_t* q, float* s, void* stream) {
     using namespace moe;
     const char* what = "moe_quant_act_int8";

@@ -251,6 +251,24 @@ __device__ __forceinline__ u32x4_t i8x8_to_f16_perm(uint32_t d0, uint32_t d1) {
     return r;
 }
 
+// 8 int16 (4 dwords, elements in order) -> their high bytes (signed) and low
+// bytes (unsigned) as exact fp16 integers in pair order, q = 256 * hi + lo.
+__device__ __forceinline__ void i16x8_to_f16_hilo(u32x4_t d, u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t A = d[p >> 1], B = d[2 + (p >> 1)];  // elements p and p + 4
+        const uint32_t hb = 2 * (p & 1) + 1, lb = 2 * (p & 1);
+        uint32_t th = __builtin_amdgcn_perm(B, A, 0x0C000C00u | ((4 + hb) << 16) | hb);
+        uint32_t tl = __builtin_amdgcn_perm(B, A, 0x0C000C00u | ((4 + lb) << 16) | lb);
+        th = (th ^ 0x00800080u) | 0x64006400u;  // fp16 1024 + (hi + 128)
+        tl = tl | 0x64006400u;                  // fp16 1024 + lo
+        hi[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, th) +
+                                                 half2_t{(_Float16)-1152.0f, (_Float16)-1152.0f});
+        lo[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, tl) +
+                                                 half2_t{(_Float16)-1024.0f, (_Float16)-1024.0f});
+    }
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
 // (lgkmcnt) but not for its global loads, so prefetched weights and the next
 // activation chunk stay in flight across it (a full __syncthreads also drains
@@ -274,15 +292,18 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
     static_assert(CB == 2 || CB == 4, "column blocks per wave");
     static_assert(CB == 4 || MODE != MOE_MODE_EXACT_I8, "exact mode quantises 32 output columns per wave");
     constexpr int BM = 16 * MB;
-    constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
+    constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8 || MODE == MOE_MODE_EXACT_I16;
+    constexpr bool ACT16 = MODE == MOE_MODE_EXACT_I16;  // 16-bit activation codes: two fp16 planes
     constexpr bool F16P = MODE == MOE_MODE_BF16_F16P;  // activations already in the fp16 staging format
     constexpr bool GATEUP = OP == 0;
     // activation staging: a bf16 row chunk is 16 pieces of 16 B, an int8 row chunk 8
-    constexpr int PIECES = EXACT ? 8 : 16;
+    constexpr int PIECES = (EXACT && !ACT16) ? 8 : 16;
     constexpr int A_ITERS = BM * PIECES / 256;
     static_assert(BM * PIECES % 256 == 0 && A_ITERS * (64 / PIECES) * 4 == BM, "staging pieces must tile the workgroup");
 
     __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][kAStride];
+    // 16-bit activations: As holds the high-byte plane, As2 the low-byte plane
+    __shared__ __attribute__((aligned(16))) _Float16 As2[ACT16 ? 2 : 1][ACT16 ? BM : 1][kAStride];
     __shared__ __attribute__((aligned(16))) float SXs[2][4][EXACT ? BM : 1];
     __shared__ int32_t rowsrc[BM];
 
@@ -333,7 +354,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
     // lanes x 16 contiguous bytes per row), so every cache line it touches is used
     // whole; wave w moves rows A_ITERS*RPI*w + RPI*it + lane/PIECES.  Rows past the
     // tile take the tile's first row.
-    constexpr int PIECE_ELEMS = EXACT ? 16 : 8;
+    constexpr int PIECE_ELEMS = (EXACT && !ACT16) ? 16 : 8;
     constexpr int RPI = 64 / PIECES;
     auto srow_of = [&](int it) { return A_ITERS * RPI * wave + RPI * it + lane / PIECES; };
     int aoff[A_ITERS];
@@ -373,7 +394,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
             if (!staged(nact, it)) continue;
-            if (!EXACT)
+            if (!EXACT || ACT16)
                 Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + aoff[it] + c * kKC);
             else
                 Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + aoff[it] + c * kKC);
@@ -388,7 +409,12 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
             if (!staged(nact, it)) continue;
             const int row = srow_of(it);
             const int piece = lane % PIECES;
-            if (!EXACT) {
+            if (ACT16) {
+                u32x4_t hi, lo;
+                i16x8_to_f16_hilo(Aq[it], hi, lo);
+                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = hi;
+                *reinterpret_cast<u32x4_t*>(&As2[ACT16 ? buf : 0][ACT16 ? row : 0][piece * 8]) = lo;
+            } else if (!EXACT) {
                 *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = F16P ? Aq[it] : bf16x8_to_f16_perm(Aq[it]);
             } else {
                 *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16]) = i8x8_to_f16_perm(Aq[it][0], Aq[it][1]);
@@ -454,23 +480,34 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
         auto sxv = [&](int st) __attribute__((always_inline)) {
             return *reinterpret_cast<const f32x4_t*>(&SXs[buf][st / NACT][16 * (st % NACT) + 4 * j]);
         };
-        half8_t afr[NS];
+        auto frag2 = [&](int st) __attribute__((always_inline)) {
+            return *reinterpret_cast<const half8_t*>(&As2[ACT16 ? buf : 0][ACT16 ? 16 * (st % NACT) + r : 0]
+                                                         [ACT16 ? 32 * (st / NACT) + 8 * j : 0]);
+        };
+        half8_t afr[NS], afr2[ACT16 ? NS : 1];
         f32x4_t sxr[NS];
 #pragma unroll
         for (int q = 0; q < PF && q < NS; ++q) {
             afr[q] = frag(q);
+            if constexpr (ACT16) afr2[q] = frag2(q);
             if constexpr (EXACT) sxr[q] = sxv(q);
         }
         half8_t bfa[CB], bfb[CB];
         dequant_step(sl, 0, bfa);
         f32x4_t d[2][CB];
+        f32x4_t d2[ACT16 ? 2 : 1][CB];  // 16-bit activations: the low-byte plane's results
         auto fold = [&](auto sc) __attribute__((always_inline)) {
             constexpr int st = decltype(sc)::value;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[st % NACT][cb][i] = __builtin_fmaf(d[st & 1][cb][i], sxr[st][i], acc[st % NACT][cb][i]);
+                for (int i = 0; i < 4; ++i) {
+                    // s_w * G: exact for 8-bit codes; for 16-bit codes the two planes'
+                    // exact results combine with one rounding, 256 * hi + lo
+                    float sg = d[st & 1][cb][i];
+                    if constexpr (ACT16) sg = __builtin_fmaf(sg, 256.0f, d2[st & 1][cb][i]);
+                    acc[st % NACT][cb][i] = __builtin_fmaf(sg, sxr[st][i], acc[st % NACT][cb][i]);
+                }
                 // an empty statement that reads and writes the sums keeps the folds
                 // here, between the products, instead of all at the chunk's end
                 asm volatile("" : "+v"(acc[st % NACT][cb]));
@@ -482,6 +519,7 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
             constexpr int mb = st % NACT;
             if constexpr (st + PF < NS) {
                 afr[st + PF] = frag(st + PF);
+                if constexpr (ACT16) afr2[st + PF] = frag2(st + PF);
                 if constexpr (EXACT) sxr[st + PF] = sxv(st + PF);
             }
             if constexpr (mb == 0 && g < 3) dequant_step(sl, g + 1, (g & 1) ? bfa : bfb);
@@ -490,9 +528,13 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
             for (int cb = 0; cb < CB; ++cb) {
                 if constexpr (!EXACT)
                     acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[st], cur[cb], acc[mb][cb], 0, 0, 0);
-                else
+                else {
                     d[st & 1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[st], cur[cb],
                                                                            f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    if constexpr (ACT16)
+                        d2[st & 1][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            afr2[st], cur[cb], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                }
             }
             if constexpr (EXACT && st > 0) fold(std::integral_constant<int, st - 1>{});
             // bf16: VALU work may move across products; exact: nothing does (the
@@ -573,11 +615,17 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
                     float amax = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
                     for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-                    const float s = (amax == 0.0f) ? 0.0f : amax / 127.0f;
+                    const float s = (amax == 0.0f) ? 0.0f : amax / (ACT16 ? 32767.0f : 127.0f);
                     if (ok) {
-                        int8_t* o = static_cast<int8_t*>(a.out) + orow * N + n0 + r;
-                        o[0] = (int8_t)moe_quant_i8(h0, s);
-                        o[16] = (int8_t)moe_quant_i8(h1, s);
+                        if constexpr (ACT16) {
+                            int16_t* o = static_cast<int16_t*>(a.out) + orow * N + n0 + r;
+                            o[0] = (int16_t)moe_quant_i16(h0, s);
+                            o[16] = (int16_t)moe_quant_i16(h1, s);
+                        } else {
+                            int8_t* o = static_cast<int8_t*>(a.out) + orow * N + n0 + r;
+                            o[0] = (int8_t)moe_quant_i8(h0, s);
+                            o[16] = (int8_t)moe_quant_i8(h1, s);
+                        }
                         if (r == 0) a.out_scale[orow * (N / 32) + grp] = s;
                     }
                 }
@@ -1088,7 +1136,7 @@ void launch_tiles(GroupedArgs a, int S, hipStream_t st) {
     a.n_chunks = OP == 0 ? a.N / (32 * CB) : a.N / (64 * CB);
     const long tiles = ((long)S + (long)a.E * (16 * MB - 1)) / (16 * MB) + 1;
     const dim3 grid(8 * moe::per_xcd(tiles * a.n_chunks));
-    if constexpr (MODE == MOE_MODE_EXACT_I8)
+    if constexpr (MODE == MOE_MODE_EXACT_I8 || MODE == MOE_MODE_EXACT_I16)
         hipLaunchKernelGGL((k_grouped_exact<MODE, OP, MB, CB>), grid, dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL((k_grouped<MODE, OP, MB, CB>), grid, dim3(256), 0, st, a);
@@ -1105,34 +1153,39 @@ void launch_tiles32(GroupedArgs a, int S, hipStream_t st) {
 template <int MODE, int OP>
 int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
     // exact mode keeps its accumulators in VGPRs (the group folds are VALU work)
-    // and carries the s_x tile: at most 4 row blocks
-    constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
-    const int mb = EXACT ? min(pick_mb(S, a.E), 4) : pick_mb(S, a.E);
-    if (mb == 1) {
-        a.n_chunks = OP == 0 ? a.N / 128 : a.N / 256;
-        const long tiles = ((long)S + (long)a.E * 15) / 16 + 1;
-        hipLaunchKernelGGL((k_grouped_skinny<MODE, OP, EXACT ? kSkinnyDepthExact : kSkinnyDepth>),
-                           dim3(8 * moe::per_xcd(tiles * a.n_chunks)), dim3(256), 0, st, a);
-        return moe::launch_status(what);
-    }
-    if constexpr (EXACT) {
-        if (mb == 2) launch_tiles<MODE, OP, 2, 4>(a, S, st);
-        else launch_tiles<MODE, OP, 4, 4>(a, S, st);
+    // and carries the s_x tile: at most 4 row blocks; with 16-bit activations
+    // (two operand planes) always 2, whatever the batch
+    if constexpr (MODE == MOE_MODE_EXACT_I16) {
+        launch_tiles<MODE, OP, 2, 4>(a, S, st);
     } else {
-        switch (mb) {
-        case 2: launch_tiles<MODE, OP, 2, pick_cb(MODE, 2)>(a, S, st); break;
-        case 4: launch_tiles<MODE, OP, 4, pick_cb(MODE, 4)>(a, S, st); break;
-        case 6: launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st); break;
-        default: {
-            // the 32x32 kernel addresses activation rows with 32-bit byte offsets
-            const size_t act_rows = OP == 0 ? (size_t)S / (size_t)a.k : (size_t)S;
-            const size_t act_bytes = act_rows * (size_t)a.K * 2;
-            a.act_bytes = (uint32_t)act_bytes;
-            if (act_bytes >= ((size_t)1 << 32)) launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st);
-            else if (mb == 8) launch_tiles32<MODE, OP, 4>(a, S, st);
-            else launch_tiles32<MODE, OP, 6>(a, S, st);
-            break;
+        constexpr bool EXACT = MODE == MOE_MODE_EXACT_I8;
+        const int mb = EXACT ? min(pick_mb(S, a.E), 4) : pick_mb(S, a.E);
+        if (mb == 1) {
+            a.n_chunks = OP == 0 ? a.N / 128 : a.N / 256;
+            const long tiles = ((long)S + (long)a.E * 15) / 16 + 1;
+            hipLaunchKernelGGL((k_grouped_skinny<MODE, OP, EXACT ? kSkinnyDepthExact : kSkinnyDepth>),
+                               dim3(8 * moe::per_xcd(tiles * a.n_chunks)), dim3(256), 0, st, a);
+            return moe::launch_status(what);
         }
+        if constexpr (EXACT) {
+            if (mb == 2) launch_tiles<MODE, OP, 2, 4>(a, S, st);
+            else launch_tiles<MODE, OP, 4, 4>(a, S, st);
+        } else {
+            switch (mb) {
+            case 2: launch_tiles<MODE, OP, 2, pick_cb(MODE, 2)>(a, S, st); break;
+            case 4: launch_tiles<MODE, OP, 4, pick_cb(MODE, 4)>(a, S, st); break;
+            case 6: launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st); break;
+            default: {
+                // the 32x32 kernel addresses activation rows with 32-bit byte offsets
+                const size_t act_rows = OP == 0 ? (size_t)S / (size_t)a.k : (size_t)S;
+                const size_t act_bytes = act_rows * (size_t)a.K * 2;
+                a.act_bytes = (uint32_t)act_bytes;
+                if (act_bytes >= ((size_t)1 << 32)) launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st);
+                else if (mb == 8) launch_tiles32<MODE, OP, 4>(a, S, st);
+                else launch_tiles32<MODE, OP, 6>(a, S, st);
+                break;
+            }
+            }
         }
     }
     return moe::launch_status(what);
@@ -1140,7 +1193,8 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
 
 int check_common(const char* what, int mode, int T, int k, int E) {
     using namespace moe;
-    if (mode != MOE_MODE_BF16 && mode != MOE_MODE_EXACT_I8 && mode != MOE_MODE_BF16_F16P)
+    if (mode != MOE_MODE_BF16 && mode != MOE_MODE_EXACT_I8 && mode != MOE_MODE_BF16_F16P &&
+        mode != MOE_MODE_EXACT_I16)
         return fail(MOE_ERR_INVALID_ARG, "%s: mode %d", what, mode);
     if (T < 0 || k <= 0 || E <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes", what);
     if (E > 1024 || k > 16 || k > E || (long)T * k >= (1L << 31))
@@ -1164,7 +1218,7 @@ extern "C" int moe_int4_grouped_swiglu(int mode, const void* act, const float* a
     if (T == 0) return MOE_OK;
     if (!act || !gate_packed || !gate_scale || !up_packed || !up_scale || !offsets || !sorted_slot || !h)
         return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
-    const bool exact = mode == MOE_MODE_EXACT_I8;
+    const bool exact = mode == MOE_MODE_EXACT_I8 || mode == MOE_MODE_EXACT_I16;
     if (exact && (!act_scale || !h_scale))
         return fail(MOE_ERR_INVALID_ARG, "%s: exact mode needs act_scale and h_scale", what);
     if (!exact && (act_scale || h_scale))
@@ -1188,6 +1242,7 @@ extern "C" int moe_int4_grouped_swiglu(int mode, const void* act, const float* a
     a.out = h;
     a.out_scale = h_scale;
     hipStream_t st = as_stream(stream);
+    if (mode == MOE_MODE_EXACT_I16) return launch_grouped<MOE_MODE_EXACT_I16, 0>(a, T * k, st, what);
     if (exact) return launch_grouped<MOE_MODE_EXACT_I8, 0>(a, T * k, st, what);
     if (mode == MOE_MODE_BF16_F16P) return launch_grouped<MOE_MODE_BF16_F16P, 0>(a, T * k, st, what);
     return launch_grouped<MOE_MODE_BF16, 0>(a, T * k, st, what);
@@ -1205,7 +1260,7 @@ extern "C" int moe_int4_grouped_down(int mode, const void* h, const float* h_sca
     if (T == 0) return MOE_OK;
     if (!h || !down_packed || !down_scale || !offsets || !y)
         return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
-    const bool exact = mode == MOE_MODE_EXACT_I8;
+    const bool exact = mode == MOE_MODE_EXACT_I8 || mode == MOE_MODE_EXACT_I16;
     if (exact && !h_scale) return fail(MOE_ERR_INVALID_ARG, "%s: exact mode needs h_scale", what);
     if (!exact && h_scale) return fail(MOE_ERR_INVALID_ARG, "%s: bf16 mode takes no scales", what);
     if (!aligned16(h) || !aligned16(down_packed) || (exact && !aligned16(h_scale)))
@@ -1222,6 +1277,7 @@ extern "C" int moe_int4_grouped_down(int mode, const void* h, const float* h_sca
     a.N = H;
     a.out = y;
     hipStream_t st = as_stream(stream);
+    if (mode == MOE_MODE_EXACT_I16) return launch_grouped<MOE_MODE_EXACT_I16, 1>(a, T * k, st, what);
     if (exact) return launch_grouped<MOE_MODE_EXACT_I8, 1>(a, T * k, st, what);
     if (mode == MOE_MODE_BF16_F16P) return launch_grouped<MOE_MODE_BF16_F16P, 1>(a, T * k, st, what);
     return launch_grouped<MOE_MODE_BF16, 1>(a, T * k, st, what);

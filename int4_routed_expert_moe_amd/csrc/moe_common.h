@@ -91,4 +91,12 @@ __device__ __forceinline__ int32_t moe_quant_i8(float v, float s) {
     return (int32_t)r;
 }
 
+// The same quantiser for 16-bit codes: clamp to +-32767.
+__device__ __forceinline__ int32_t moe_quant_i16(float v, float s) {
+    if (s == 0.0f) return 0;
+    float r = __builtin_rintf(v / s);
+    r = r > 32767.0f ? 32767.0f : (r < -32767.0f ? -32767.0f : r);
+    return (int32_t)r;
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (MOE_WAVE - 1)); }

@@ -51,7 +51,11 @@ class MoELayer:
     def __init__(self, cfg: dict, router_w, router_b, experts: dict, shared: dict | None = None,
                  latent: dict | None = None):
         self.cfg = dict(cfg)
-        self.mode = _m.MOE_MODE_EXACT_I8 if cfg["mode"] == "exact" else _m.MOE_MODE_BF16
+        # exact mode: 8-bit activation codes, or 16-bit with act_bits = 16
+        if cfg["mode"] == "exact":
+            self.mode = _m.MOE_MODE_EXACT_I16 if int(cfg.get("act_bits", 8)) == 16 else _m.MOE_MODE_EXACT_I8
+        else:
+            self.mode = _m.MOE_MODE_BF16
         self.router_w = router_w
         self.router_b = router_b
         self.ex = prepack_experts(experts)
@@ -66,7 +70,7 @@ class MoELayer:
         self._ws = {}
         self._side = None
         self.device = router_w.device
-        if self.mode == _m.MOE_MODE_EXACT_I8 and (shared is not None or latent is not None):
+        if self.mode in (_m.MOE_MODE_EXACT_I8, _m.MOE_MODE_EXACT_I16) and (shared is not None or latent is not None):
             raise ValueError("exact mode is defined for the routed experts alone")
 
     @classmethod
@@ -96,7 +100,8 @@ class MoELayer:
             return self._ws[T]
         dev, E, k, H, I, Kin = self.device, self.E, self.k, self.H, self.I, self.Kin
         S = T * k
-        exact = self.mode == _m.MOE_MODE_EXACT_I8
+        exact = self.mode in (_m.MOE_MODE_EXACT_I8, _m.MOE_MODE_EXACT_I16)
+        codes = torch.int16 if self.mode == _m.MOE_MODE_EXACT_I16 else torch.int8
         staged = not exact and T >= self.STAGED_ACT_MIN_T
         w = {
             "route_ws": torch.empty(max(1, _m.moe_route_workspace_bytes(T, self.H, E)), dtype=torch.uint8, device=dev),
@@ -106,7 +111,7 @@ class MoELayer:
             "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
             "sorted_slot": torch.empty(S, dtype=torch.int32, device=dev),
             "slot_pos": torch.empty(S, dtype=torch.int32, device=dev),
-            "h": torch.empty((S, I), dtype=torch.int8 if exact else torch.float16 if staged else torch.bfloat16,
+            "h": torch.empty((S, I), dtype=codes if exact else torch.float16 if staged else torch.bfloat16,
                              device=dev),
             "h_scale": torch.empty((S, I // 32), dtype=torch.float32, device=dev) if exact else None,
             "y": torch.empty((S, Kin), dtype=torch.float32 if exact else torch.bfloat16, device=dev),
@@ -115,7 +120,7 @@ class MoELayer:
         if staged:
             w["act16"] = torch.empty((T, Kin), dtype=torch.float16, device=dev)
         if exact:
-            w["qx"] = torch.empty((T, Kin), dtype=torch.int8, device=dev)
+            w["qx"] = torch.empty((T, Kin), dtype=codes, device=dev)
             w["sx"] = torch.empty((T, Kin // 32), dtype=torch.float32, device=dev)
         dense_bytes = 0
         if self.shared is not None:
@@ -192,9 +197,13 @@ class MoELayer:
             if side is None:
                 self._shared_expert(x, w, mark)
             shared_out = w["shared_out"]
-        if self.mode == _m.MOE_MODE_EXACT_I8:
-            _m.moe_quant_act_int8(act, w["qx"], w["sx"])
-            mark("moe_quant_act_int8")
+        if self.mode in (_m.MOE_MODE_EXACT_I8, _m.MOE_MODE_EXACT_I16):
+            if self.mode == _m.MOE_MODE_EXACT_I16:
+                _m.moe_quant_act_int16(act, w["qx"], w["sx"])
+                mark("moe_quant_act_int16")
+            else:
+                _m.moe_quant_act_int8(act, w["qx"], w["sx"])
+                mark("moe_quant_act_int8")
             _m.moe_int4_grouped_swiglu(self.mode, w["qx"], w["sx"], ex["wg"], ex["sg"], ex["wu"], ex["su"],
                                        w["offsets"], w["sorted_slot"], T, k, E, Kin, I, w["h"], w["h_scale"])
             gmode = self.mode
@@ -216,8 +225,10 @@ class MoELayer:
         mark("moe_int4_grouped_down")
         if side is not None:
             torch.cuda.current_stream().wait_event(self._ev_join)
+        # the combine sees fp32 y in either exact mode
+        cmode = _m.MOE_MODE_EXACT_I8 if self.mode == _m.MOE_MODE_EXACT_I16 else self.mode
         if self.latent is None:
-            _m.moe_combine(self.mode, w["y"], w["slot_pos"], w["topk_w"], shared_out, T, k, H, w["out"])
+            _m.moe_combine(cmode, w["y"], w["slot_pos"], w["topk_w"], shared_out, T, k, H, w["out"])
             mark("moe_combine")
         else:
             _m.moe_combine(self.mode, w["y"], w["slot_pos"], w["topk_w"], None, T, k, Kin, w["routed"])

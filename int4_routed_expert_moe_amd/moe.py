@@ -30,6 +30,7 @@ MOE_ERR_LAUNCH = -4
 MOE_MODE_BF16 = 0
 MOE_MODE_EXACT_I8 = 1
 MOE_MODE_BF16_F16P = 2
+MOE_MODE_EXACT_I16 = 3
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -46,6 +47,7 @@ EXPORTS = {
     "moe_quant_act_int8": ([_P, _I, _I, _P, _P, _P], _I),
     "moe_int4_prepack": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "moe_act_f16p": ([_P, _I, _I, _P, _P], _I),
+    "moe_quant_act_int16": ([_P, _I, _I, _P, _P, _P], _I),
     "moe_int4_grouped_swiglu": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_int4_grouped_down": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_I, _P, _P, _P, _P, _I, _I, _I, _P, _P], _I),
@@ -149,6 +151,14 @@ def moe_quant_act_int8(x, q, s):
     _check("moe_quant_act_int8", _lib.moe_quant_act_int8(_ptr(x), M, K, _ptr(q), _ptr(s), _stream()))
 
 
+def moe_quant_act_int16(x, q, s):
+    M, K = x.shape
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(q, torch.int16, (M, K), "q")
+    _need(s, torch.float32, (M, K // 32), "s")
+    _check("moe_quant_act_int16", _lib.moe_quant_act_int16(_ptr(x), M, K, _ptr(q), _ptr(s), _stream()))
+
+
 def moe_int4_prepack(packed, scale, packed_out, scale_out):
     """Checkpoint-layout expert matrices [E, N, K/2] + [E, N, K/32] -> the fragment layout
     the grouped GEMMs read (same shapes and dtypes, out of place)."""
@@ -164,7 +174,9 @@ def moe_int4_prepack(packed, scale, packed_out, scale_out):
                                                      _ptr(scale_out), _stream()))
 
 
-_ACT_DTYPE = {MOE_MODE_BF16: torch.bfloat16, MOE_MODE_EXACT_I8: torch.int8, MOE_MODE_BF16_F16P: torch.float16}
+_ACT_DTYPE = {MOE_MODE_BF16: torch.bfloat16, MOE_MODE_EXACT_I8: torch.int8, MOE_MODE_BF16_F16P: torch.float16,
+              MOE_MODE_EXACT_I16: torch.int16}
+_EXACT_MODES = (MOE_MODE_EXACT_I8, MOE_MODE_EXACT_I16)
 
 
 def moe_act_f16p(x, out):
@@ -188,11 +200,11 @@ def moe_int4_grouped_swiglu(mode, act, act_scale, gate_packed, gate_scale, up_pa
                            (offsets, torch.int32, (E + 1,), "offsets"),
                            (sorted_slot, torch.int32, (T * k,), "sorted_slot")):
         _need(t, dt, shp, nm)
-    if mode != MOE_MODE_EXACT_I8:
+    if mode not in _EXACT_MODES:
         _need(h, _ACT_DTYPE.get(mode, torch.bfloat16), (T * k, I), "h")
     else:
         _need(act_scale, torch.float32, (T, H // 32), "act_scale")
-        _need(h, torch.int8, (T * k, I), "h")
+        _need(h, _ACT_DTYPE[mode], (T * k, I), "h")
         _need(h_scale, torch.float32, (T * k, I // 32), "h_scale")
     _check("moe_int4_grouped_swiglu", _lib.moe_int4_grouped_swiglu(
         mode, _ptr(act), _ptr(act_scale), _ptr(gate_packed), _ptr(gate_scale), _ptr(up_packed), _ptr(up_scale),
@@ -204,7 +216,7 @@ def moe_int4_grouped_down(mode, h, h_scale, down_packed, down_scale, offsets, T,
     _need(down_packed, torch.uint8, (E, H, I // 2), "down_packed")
     _need(down_scale, torch.bfloat16, (E, H, I // 32), "down_scale")
     _need(offsets, torch.int32, (E + 1,), "offsets")
-    if mode != MOE_MODE_EXACT_I8:
+    if mode not in _EXACT_MODES:
         _need(y, torch.bfloat16, (T * k, H), "y")
     else:
         _need(h_scale, torch.float32, (T * k, I // 32), "h_scale")

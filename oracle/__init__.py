@@ -493,11 +493,13 @@ def layer_tokens(inp, tokens, topk_idx=None, topk_w=None, want_intermediates=Fal
     experts = idx.reshape(-1)
     inter = {"idx": idx, "w": w}
     if cfg["mode"] == "exact":
-        qx, sx = quant_act_int8(xr)
+        act16 = int(cfg.get("act_bits", 8)) == 16
+        qx, sx = (quant_act_int16 if act16 else quant_act_int8)(xr)
         qrows = np.repeat(qx, k, axis=0)
         srows = np.repeat(sx, k, axis=0)
-        r = experts_exact(qrows, srows, experts, inp["experts"],
-                          want=("g", "u", "qh", "sh", "y") if want_intermediates else ("y",))
+        r = (experts_exact16 if act16 else experts_exact)(
+            qrows, srows, experts, inp["experts"],
+            want=("g", "u", "qh", "sh", "y") if want_intermediates else ("y",))
         out = combine_f32(r["y"].reshape(n, k, -1), w)
         inter.update(r)
         inter.update({"qx": qx, "sx": sx})

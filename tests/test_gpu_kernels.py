@@ -173,6 +173,21 @@ def test_quant_act_bitexact(m, M, K, seed):
     np.testing.assert_array_equal(s.cpu().numpy(), rs)
 
 
+@pytest.mark.parametrize("M,K,seed", [(1, 32, 0), (37, 256, 1), (64, 7168, 2)])
+def test_quant_act16_bitexact(m, M, K, seed):
+    say(f"quant16 M={M} K={K}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (M, K))
+    x[0, :32] = 0  # a zero group
+    rq, rs = oracle.quant_act_int16(x)
+    q = torch.empty((M, K), dtype=torch.int16, device="cuda")
+    s = torch.empty((M, K // 32), dtype=torch.float32, device="cuda")
+    m.moe_quant_act_int16(bf16_dev(x), q, s)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+
+
 @pytest.mark.parametrize("M,N,K,seed", [(16, 16, 32, 0), (48, 32, 7168, 1), (16, 64, 2048, 2)])
 def test_group_sums_bitexact(m, M, N, K, seed):
     say(f"group sums M={M} N={N} K={K}")
@@ -361,6 +376,39 @@ def test_act_f16p_layout(m, rows, K, seed):
     m.moe_act_f16p(bf16_dev(x), out)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), _f16p_ref(x))
+
+
+@pytest.mark.parametrize("T,H,I,E,k,skew,seed", [
+    (64, 256, 128, 16, 2, False, 0),
+    (300, 256, 128, 4, 2, True, 1),      # several tiles per expert, empty experts
+    (45, 512, 256, 5, 3, False, 2),      # ragged tiles
+    (200, 512, 256, 8, 2, False, 3),
+])
+def test_grouped_exact16_bitexact(m, T, H, I, E, k, skew, seed):
+    """Exact mode with 16-bit activation codes: q_h, s_h and y bit-exact."""
+    say(f"grouped exact16 T={T} H={H} I={I} E={E} k={k}")
+    g = np.random.default_rng(seed)
+    W = _expert_set(g, E, H, I)
+    x = _rand_bf16(g, (T, H))
+    idx, w = _routing(g, T, E, k, skew)
+    counts, offsets, ss, sp = oracle.permute(idx, E)
+    S = T * k
+    qx, sx = oracle.quant_act_int16(x)
+    ref = oracle.experts_exact16(qx[ss // k], sx[ss // k], idx.reshape(-1)[ss], W, want=("qh", "sh", "y"))
+    D = _dev_experts(W)
+    off_d = torch.from_numpy(offsets).cuda()
+    qh = torch.empty((S, I), dtype=torch.int16, device="cuda")
+    sh = torch.empty((S, I // 32), dtype=torch.float32, device="cuda")
+    y = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    m.moe_int4_grouped_swiglu(m.MOE_MODE_EXACT_I16, torch.from_numpy(qx).cuda(), torch.from_numpy(sx).cuda(),
+                              D["wg"], D["sg"], D["wu"], D["su"], off_d, torch.from_numpy(ss).cuda(), T, k, E, H, I,
+                              qh, sh)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sh.cpu().numpy(), ref["sh"])
+    np.testing.assert_array_equal(qh.cpu().numpy(), ref["qh"])
+    m.moe_int4_grouped_down(m.MOE_MODE_EXACT_I16, qh, sh, D["wd"], D["sd"], off_d, T, k, E, I, H, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), ref["y"])
 
 
 # ---------------------------------------------------------------- dense pieces

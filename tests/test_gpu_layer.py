@@ -136,3 +136,37 @@ def test_layer_group_limited_routing():
     ref, inter = oracle.layer_tokens(inp, np.arange(cfg["T"]), want_intermediates=True)
     terms = (inter["routed"], inter["shared"]) if inp.get("shared") is not None else ()
     assert_bf16_close(np_bf16(out), ref, "out", addends=terms)
+
+
+def test_layer_exact16_on_skewed_routing():
+    """The skewed exact workload with 16-bit activation codes: routing, the codes,
+    h and y bit-exact on a token sample, the output within 1e-5."""
+    from int4_routed_expert_moe_amd.layer import MoELayer
+    base = inputs(4)
+    inp = dict(base)
+    inp["cfg"] = dict(base["cfg"], act_bits=16)
+    cfg = inp["cfg"]
+    T, k = cfg["T"], cfg["k"]
+    L = MoELayer.from_numpy(inp, "cuda")
+    say("layer forward workload 4 with 16-bit activation codes")
+    out = L.forward(bf16_dev(inp["x"]))
+    torch.cuda.synchronize()
+    ws = L.workspace(T)
+    ridx = ws["topk_idx"].cpu().numpy()
+    rw = ws["topk_w"].cpu().numpy()
+    oidx, ow = oracle.route(inp["x"], inp["router_w"], inp["router_b"], k, True)
+    np.testing.assert_array_equal(ridx, oidx)
+    np.testing.assert_array_equal(rw, ow)
+    toks = synthetic.token_sample(cfg, 12)
+    say(f"oracle on {len(toks)} tokens of workload 4 (16-bit codes)")
+    ref, inter = oracle.layer_tokens(inp, toks, topk_idx=oidx, topk_w=ow, want_intermediates=True)
+    rp = ws["slot_pos"].cpu().numpy()
+    pos = rp[(toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)]
+    np.testing.assert_array_equal(ws["qx"].cpu().numpy()[toks], inter["qx"])
+    np.testing.assert_array_equal(ws["sx"].cpu().numpy()[toks], inter["sx"])
+    np.testing.assert_array_equal(ws["h"].cpu().numpy()[pos], inter["qh"])
+    np.testing.assert_array_equal(ws["h_scale"].cpu().numpy()[pos], inter["sh"])
+    np.testing.assert_array_equal(ws["y"].cpu().numpy()[pos], inter["y"])
+    got = out.cpu().numpy()[toks]
+    assert_f32_close(got, ref, "exact16 out", 1e-5)
+    np.testing.assert_array_equal(got, ref)
