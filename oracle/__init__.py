@@ -90,6 +90,7 @@ def _declare(L):
     L.oracle_group_sums16.argtypes = [P, P, I32, I32, I32, P, P]
     L.oracle_exact_linear16.argtypes = [P, P, P, P, I32, I32, I32, P]
     L.oracle_experts_exact16.argtypes = [P, P, P, I32, I32, I32] + [P] * 6 + [P] * 5
+    L.oracle_exact_linear_i8w.argtypes = [P, P, P, P, I32, I32, I32, P]
     for name in ("oracle_exp_ref_n", "oracle_sigmoid_ref_n", "oracle_silu_ref_n",
                  "oracle_f64_to_bf16_n", "oracle_f32_to_bf16_n"):
         getattr(L, name).argtypes = [P, I32, P]
@@ -100,7 +101,7 @@ def _declare(L):
                "oracle_quant_f32_int8", "oracle_quant_act_int8", "oracle_group_sums",
                "oracle_exact_linear", "oracle_experts_exact", "oracle_combine_f32",
                "oracle_topk_grouped_from_scores", "oracle_quant_act_int16", "oracle_group_sums16",
-               "oracle_exact_linear16", "oracle_experts_exact16"):
+               "oracle_exact_linear16", "oracle_experts_exact16", "oracle_exact_linear_i8w"):
         getattr(L, fn).restype = None
 
 
@@ -446,6 +447,19 @@ def experts_exact16(qx, sx, experts, W, want=("y",)):
         if v is not None:
             out[name] = v
     return out
+
+
+def exact_linear_i8w(qx, sx, qw, sw):
+    """ExactLinear with 8-bit weights: int8 codes and fp32 group scales on both sides."""
+    qx = _c(qx, np.int8)
+    sx = _c(sx, np.float32)
+    qw = _c(qw, np.int8)
+    sw = _c(sw, np.float32)
+    M, K = qx.shape
+    N = qw.shape[0]
+    y = np.empty((M, N), dtype=np.float32)
+    lib().oracle_exact_linear_i8w(_p(qx), _p(sx), _p(qw), _p(sw), M, N, K, _p(y))
+    return y
 
 
 def combine_f32(y, w):

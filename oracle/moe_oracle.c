@@ -733,6 +733,34 @@ void oracle_experts_exact16(const int16_t* qx, const float* sx, const int32_t* e
     }
 }
 
+/* ------------------------------------------------------------------------- */
+/* ExactLinear with 8-bit weights (adaptation page, "The proposed            */
+/* substitution": ExactLinear.from_weight with bits 4 or 8 and group size 32; */
+/* the class body is not on the pages).  Readings: the weights are quantised  */
+/* like the activations, per row and group of 32 with an fp32 scale amax/127  */
+/* and codes clamped to +-127; each group's int8 x int8 dot product is an     */
+/* exact int32 (|G| <= 32 * 127 * 127); the fold is the exact mode's,         */
+/*   acc = fmaf(fl32(s_w * (float)G), s_x, acc), groups ascending, from 0.    */
+/* y [M, N] fp32.                                                             */
+/* ------------------------------------------------------------------------- */
+void oracle_exact_linear_i8w(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw, int M, int N,
+                             int K, float* y) {
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            const int8_t* xr = qx + (size_t)m * K;
+            const int8_t* wr = qw + (size_t)n * K;
+            float acc = 0.0f;
+            for (int g = 0; g < K / 32; ++g) {
+                int32_t G = 0;
+                for (int i = g * 32; i < g * 32 + 32; ++i) G += (int)wr[i] * (int)xr[i];
+                const float cw = sw[(size_t)n * (K / 32) + g] * (float)G;
+                acc = fmaf(cw, sx[(size_t)m * (K / 32) + g], acc);
+            }
+            y[(size_t)m * N + n] = acc;
+        }
+}
+
 /* Exact-mode combine: out[t][m] = sum_j w[t][j] * y[t][j][m] in fp32, j ascending,
  * each product rounded then added (fp32 output, no bf16 cast). */
 void oracle_combine_f32(const float* y, const float* w, int T, int k, int H, float* out) {

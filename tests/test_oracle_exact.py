@@ -234,3 +234,37 @@ def test_exact16_expert_chain():
         exact = terms.sum(axis=1)
         bound = (I // 32 + 1) * 2.0 ** -24 * np.abs(terms).sum(axis=1) * 1.01 + 1e-30
         assert np.all(np.abs(r["y"][e] - exact) <= bound)
+
+
+# ---------------------------------------------------------------- ExactLinear, 8-bit weights
+
+def test_exact_linear_i8w_power_of_two_closed_form():
+    g = np.random.default_rng(20)
+    M, N, K = 5, 7, 512
+    qx = g.integers(-40, 41, (M, K)).astype(np.int8)  # |total| <= 512 * 40 * 40 < 2^24
+    qw = g.integers(-40, 41, (N, K)).astype(np.int8)
+    total = qx.astype(np.int64) @ qw.astype(np.int64).T
+    for a, b in ((-7, -5), (0, 0), (-12, 3)):
+        sw = np.full((N, K // 32), 2.0 ** a, np.float32)
+        sx = np.full((M, K // 32), 2.0 ** b, np.float32)
+        y = oracle.exact_linear_i8w(qx, sx, qw, sw)
+        np.testing.assert_array_equal(y.astype(np.float64), total.astype(np.float64) * 2.0 ** (a + b))
+
+
+def test_exact_linear_i8w_within_fp64_bound():
+    g = np.random.default_rng(21)
+    M, N, K = 4, 9, 2048
+    x = _bf16(g.standard_normal((M, K)))
+    w = _bf16(g.standard_normal((N, K)) * 0.02)
+    qx, sx = oracle.quant_act_int8(x)
+    qw, sw = oracle.quant_act_int8(w)   # weights take the same per-row, per-group quantiser
+    y = oracle.exact_linear_i8w(qx, sx, qw, sw).astype(np.float64)
+    G = np.einsum("mgi,ngi->mng", qx.astype(np.int64).reshape(M, -1, 32), qw.astype(np.int64).reshape(N, -1, 32))
+    assert np.abs(G).max() <= 32 * 127 * 127
+    terms = G.astype(np.float64) * sw[None].astype(np.float64) * sx[:, None, :].astype(np.float64)
+    exact = terms.sum(axis=2)
+    bound = (K // 32 + 1) * 2.0 ** -24 * np.abs(terms).sum(axis=2) * 1.01
+    assert np.all(np.abs(y - exact) <= bound)
+    # and close to the unquantised product (the quantisation error, not a pin of the fold)
+    ref = refmath.bf16_to_f32(x).astype(np.float64) @ refmath.bf16_to_f32(w).astype(np.float64).T
+    assert np.max(np.abs(y - ref)) <= 0.05 * np.max(np.abs(ref))
