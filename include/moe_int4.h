@@ -128,6 +128,19 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, i
  * q = clamp(rint(x / s), -127, 127), ties to even; amax == 0 gives s = 0, q = 0.
  * x [M,K] bf16 -> q [M,K] int8, s [M,K/32] fp32.  Bit-exact. */
 int moe_quant_act_int8(const uint16_t* x, int M, int K, int8_t* q, float* s, void* stream);
+/* ExactLinear with 8-bit weights ("Kimi exact-generator adaptation", "The
+ * proposed substitution": ExactLinear.from_weight with bits 4 or 8, group size
+ * 32; the class body is not on the pages, so the reading is stated):
+ *   y[m][n] = fold over groups g ascending of
+ *             acc = fmaf(fl32(sw[n][g] * (float)G), sx[m][g], acc),  acc from 0,
+ *   G = sum over the group of qx[m][i] * qw[n][i] (exact int32).
+ * qx [M,K] int8 with sx [M,K/32] fp32 (moe_quant_act_int8 of the input);
+ * qw [N,K] int8 with sw [N,K/32] fp32 (moe_quant_act_int8 of the bf16 weight
+ * rows); y [M,N] fp32.  K a multiple of 128; qx, qw 16-byte aligned.
+ * Bit-exact. */
+int moe_exact_linear_i8w(const int8_t* qx, const float* sx, const int8_t* qw, const float* sw, int M, int N, int K,
+                         float* y, void* stream);
+
 /* The same with 16-bit codes (exact mode with act_bits = 16, the adaptation's
  * default activation width): s = amax / 32767, q = clamp(rint(x / s), +-32767)
  * -> q [M,K] int16, s [M,K/32] fp32.  Bit-exact. */

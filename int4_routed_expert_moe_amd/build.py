@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "libmoe_int4.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["status.cpp", "route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "dense.hip",
-           "group_sums.hip"]
+           "group_sums.hip", "exact_linear.hip"]
 
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 

@@ -48,6 +48,7 @@ EXPORTS = {
     "moe_int4_prepack": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "moe_act_f16p": ([_P, _I, _I, _P, _P], _I),
     "moe_quant_act_int16": ([_P, _I, _I, _P, _P, _P], _I),
+    "moe_exact_linear_i8w": ([_P, _P, _P, _P, _I, _I, _I, _P, _P], _I),
     "moe_int4_grouped_swiglu": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "moe_int4_grouped_down": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P], _I),
     "moe_combine": ([_I, _P, _P, _P, _P, _I, _I, _I, _P, _P], _I),
@@ -157,6 +158,19 @@ def moe_quant_act_int16(x, q, s):
     _need(q, torch.int16, (M, K), "q")
     _need(s, torch.float32, (M, K // 32), "s")
     _check("moe_quant_act_int16", _lib.moe_quant_act_int16(_ptr(x), M, K, _ptr(q), _ptr(s), _stream()))
+
+
+def moe_exact_linear_i8w(qx, sx, qw, sw, y):
+    """ExactLinear with 8-bit weights: y [M,N] fp32 from int8 codes and fp32 group scales."""
+    M, K = qx.shape
+    N = qw.shape[0]
+    _need(qx, torch.int8, (M, K), "qx")
+    _need(sx, torch.float32, (M, K // 32), "sx")
+    _need(qw, torch.int8, (N, K), "qw")
+    _need(sw, torch.float32, (N, K // 32), "sw")
+    _need(y, torch.float32, (M, N), "y")
+    _check("moe_exact_linear_i8w", _lib.moe_exact_linear_i8w(_ptr(qx), _ptr(sx), _ptr(qw), _ptr(sw), M, N, K,
+                                                             _ptr(y), _stream()))
 
 
 def moe_int4_prepack(packed, scale, packed_out, scale_out):

@@ -117,6 +117,10 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert _status(lib, rg, fake, fake, fake, 4, 256, 64, 9, 1, 8, 1, 1.0, fake, fake, fake, big, null) == -2
     assert _status(lib, rg, fake, fake, fake, 4, 256, 64, 4, 1, 8, 2, float("nan"), fake, fake, fake, big, null) == -1
     assert _status(lib, rg, null, null, null, 0, 256, 64, 4, 1, 8, 2, 1.0, null, null, null, ctypes.c_size_t(0), null) == 0
+    # ExactLinear 8-bit weights: K not a multiple of 128, null pointer, zero rows
+    assert _status(lib, "moe_exact_linear_i8w", fake, fake, fake, fake, 4, 64, 96, fake, null) == -2
+    assert _status(lib, "moe_exact_linear_i8w", null, fake, fake, fake, 4, 64, 128, fake, null) == -1
+    assert _status(lib, "moe_exact_linear_i8w", null, null, null, null, 0, 64, 128, null, null) == 0
     # staging conversion: K not a multiple of 8, null pointer, overlap, zero rows
     assert _status(lib, "moe_act_f16p", fake, 4, 12, P(0x200000), null) == -2
     assert _status(lib, "moe_act_f16p", null, 4, 16, P(0x200000), null) == -1

@@ -411,6 +411,30 @@ def test_grouped_exact16_bitexact(m, T, H, I, E, k, skew, seed):
     np.testing.assert_array_equal(y.cpu().numpy(), ref["y"])
 
 
+@pytest.mark.parametrize("M,N,K,seed", [(64, 64, 128, 0), (100, 200, 512, 1), (37, 96, 7168, 2),
+                                        (256, 2048, 256, 3)])
+def test_exact_linear_i8w_bitexact(m, M, N, K, seed):
+    """ExactLinear with 8-bit weights (both operands quantised on the GPU) against the oracle, bit for bit."""
+    say(f"exact linear i8w M={M} N={N} K={K}")
+    g = np.random.default_rng(seed)
+    x = _rand_bf16(g, (M, K))
+    w = _rand_bf16(g, (N, K), 0.02)
+    qx, sx = oracle.quant_act_int8(x)
+    qw, sw = oracle.quant_act_int8(w)
+    ref = oracle.exact_linear_i8w(qx, sx, qw, sw)
+    dqx = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    dsx = torch.empty((M, K // 32), dtype=torch.float32, device="cuda")
+    dqw = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    dsw = torch.empty((N, K // 32), dtype=torch.float32, device="cuda")
+    m.moe_quant_act_int8(bf16_dev(x), dqx, dsx)
+    m.moe_quant_act_int8(bf16_dev(w), dqw, dsw)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    m.moe_exact_linear_i8w(dqx, dsx, dqw, dsw, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dqw.cpu().numpy(), qw)
+    np.testing.assert_array_equal(y.cpu().numpy(), ref)
+
+
 # ---------------------------------------------------------------- dense pieces
 @pytest.mark.parametrize("M,N,K,with_add,seed", [
     (1, 64, 128, False, 0), (64, 2048, 7168, False, 1), (40, 192, 512, True, 2), (200, 256, 384, True, 3),
