@@ -32,7 +32,8 @@ def _f16p_ref(bits):
     zero (saturating at the largest finite fp16), each 8-element block stored as
     e0,e4,e1,e5,e2,e6,e3,e7.  Returns fp16 bit patterns."""
     f = bf16_to_f64(bits)
-    h = f.astype(np.float16)                       # nearest
+    with np.errstate(over="ignore"):
+        h = f.astype(np.float16)                   # nearest (values past the fp16 range become inf)
     over = np.abs(h.astype(np.float64)) > np.abs(f)  # rounded away from zero (or to inf)
     h[over] = np.nextafter(h[over], np.float16(0))
     h = h.reshape(*bits.shape[:-1], bits.shape[-1] // 8, 8)[..., _F16P_ORDER]
