@@ -8,9 +8,12 @@
 // one expert's segment of the permuted slot list; its expert and first row
 // come from the device-side offsets (no host synchronisation; the grid is
 // sized for the worst case and surplus blocks exit).  A workgroup is 4 waves;
-// each wave owns 64 weight rows (4 column blocks of 16) and all tile rows.
+// each wave owns a few column blocks of weight rows and all tile rows.  Three
+// kernels by tile height: k_grouped_skinny (at most 16 rows, decode),
+// k_grouped / k_grouped_exact (16*MB rows, 16x16x32 shape) and k_grouped32
+// (32*M32 rows, 32x32x16 shape, bf16 prefill).
 //
-// Matrix cores: v_mfma_f32_16x16x32_f16.  Weights are dequantised in
+// Matrix cores: v_mfma_f32_16x16x32_f16 (and 32x32x16).  Weights are dequantised in
 // registers to fp16 q*s: a nibble is moved to bits 6..9 of a half, its sign
 // bit flipped and an exponent OR-ed in (the half is then 16 + q + 8), and one
 // packed fma with (s, -24 s) gives q*s exactly (q*s has at most 11 significant
@@ -34,7 +37,9 @@
 // step's result is s_w * G with G the exact int32 group sum (every partial sum
 // is an integer multiple of the scale's last-bit weight below 2^24, hence
 // exact in fp32); it is folded into the row's accumulator as
-// fma(s_w*G, s_x, acc), groups ascending.
+// fma(s_w*G, s_x, acc), groups ascending.  With 16-bit activation codes the
+// high and low bytes are two exact fp16 operand planes and two steps per group
+// give s_w*G_hi and s_w*G_lo, joined exactly as fma(s_w*G_hi, 256, s_w*G_lo).
 #include <type_traits>
 
 #include "moe_common.h"
@@ -279,14 +284,16 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Tiles of up to 16*MB rows (prefill and mid-size batches; MB = 2, 4, 6, 8, 12).  A workgroup is 4
-// waves; each wave owns 64 weight rows (4 fragments) and all tile rows, so a
-// dequantised weight fragment feeds up to MB matrix-core steps.  The tile's
-// activation rows are gathered, converted to fp16 and staged in LDS one
-// 128-wide K chunk ahead (double buffer, one LDS-only barrier per chunk);
-// weights and scales run two chunks ahead in a 3-slot register ring.  Rows
-// past the tile's count read a valid row and are never written out (an
-// output row depends only on its own activation row).
+// Tiles of up to 16*MB rows on the 16x16x32 shape: bf16 tiles of 2, 4 or 6 row
+// blocks (mid-size batches) and every exact-mode tile (2 or 4 row blocks).  A
+// workgroup is 4 waves; each wave owns CB column blocks of 16 weight rows and
+// all tile rows, so a dequantised weight fragment feeds up to MB matrix-core
+// steps.  The tile's activation rows are gathered, converted to fp16 (unless
+// already in the fp16 staging format) and staged in LDS one 128-wide K chunk
+// ahead (double buffer, one LDS-only barrier per chunk); weights and scales run
+// in a register ring of RING slots.  Rows past the tile's count read a valid
+// row and are never written out (an output row depends only on its own
+// activation row).
 template <int MODE, int OP, int MB, int CB>
 __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
     static_assert(CB == 2 || CB == 4, "column blocks per wave");
@@ -1125,11 +1132,9 @@ int pick_mb(int S, int E) {
     return 12;
 }
 
-// Column blocks per wave of the tile kernel: 2 for the 6- and 8-block bf16 tiles,
-// whose accumulators then leave room for more than one workgroup per CU; the
-// 12-block tiles keep 4 (halving them doubles the LDS fragment reads per product
-// and measured slower).
-constexpr int pick_cb(int mode, int mb) { return (mode != MOE_MODE_EXACT_I8 && mb >= 6 && mb < 12) ? 2 : 4; }
+// Column blocks per wave of the bf16 tile kernel: 2 for the 6-block tiles, whose
+// accumulators then leave room for more than one workgroup per CU, else 4.
+constexpr int pick_cb(int mb) { return mb == 6 ? 2 : 4; }
 
 template <int MODE, int OP, int MB, int CB>
 void launch_tiles(GroupedArgs a, int S, hipStream_t st) {
@@ -1172,15 +1177,15 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
             else launch_tiles<MODE, OP, 4, 4>(a, S, st);
         } else {
             switch (mb) {
-            case 2: launch_tiles<MODE, OP, 2, pick_cb(MODE, 2)>(a, S, st); break;
-            case 4: launch_tiles<MODE, OP, 4, pick_cb(MODE, 4)>(a, S, st); break;
-            case 6: launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st); break;
+            case 2: launch_tiles<MODE, OP, 2, pick_cb(2)>(a, S, st); break;
+            case 4: launch_tiles<MODE, OP, 4, pick_cb(4)>(a, S, st); break;
+            case 6: launch_tiles<MODE, OP, 6, pick_cb(6)>(a, S, st); break;
             default: {
                 // the 32x32 kernel addresses activation rows with 32-bit byte offsets
                 const size_t act_rows = OP == 0 ? (size_t)S / (size_t)a.k : (size_t)S;
                 const size_t act_bytes = act_rows * (size_t)a.K * 2;
                 a.act_bytes = (uint32_t)act_bytes;
-                if (act_bytes >= ((size_t)1 << 32)) launch_tiles<MODE, OP, 6, pick_cb(MODE, 6)>(a, S, st);
+                if (act_bytes >= ((size_t)1 << 32)) launch_tiles<MODE, OP, 6, pick_cb(6)>(a, S, st);
                 else if (mb == 8) launch_tiles32<MODE, OP, 4>(a, S, st);
                 else launch_tiles32<MODE, OP, 6>(a, S, st);
                 break;
