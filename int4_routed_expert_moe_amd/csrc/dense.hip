@@ -23,7 +23,8 @@
 namespace {
 
 constexpr int kDKC = 128;
-constexpr int kDense32MinM = 256;  // rows from which the 32x32 tile kernel runs
+constexpr int kDense32MinM = 256;   // rows from which the 32x32 tile kernel runs
+constexpr int kDense32TallM = 6144; // rows from which it takes 192-row tiles
 constexpr int kDAStride = 136;  // bf16 per LDS row
 
 enum { EPI_LINEAR = 0, EPI_SWIGLU = 1 };
@@ -254,10 +255,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // operands use the same order, so each step still multiplies matching K):
 // every weight load then reads whole 128-byte lines, and the A-fragment reads
 // from LDS (272-byte rows) are free of bank conflicts.  The A tile is staged in
-// LDS one chunk ahead, a piece every 4 products; weights run one chunk ahead
-// in a 2-slot register ring; one LDS-only barrier per chunk.  Accumulator
+// LDS one chunk ahead, a piece every 4 products; weights run R-1 chunks ahead
+// in an R-slot register ring; one LDS-only barrier per chunk.  Accumulator
 // element i of lane l is row 8(i/4) + 4 kb + i%4, column c.
-template <int M32, int EPI>
+template <int M32, int EPI, int R>
 __global__ __launch_bounds__(256) void k_dense32(DenseArgs a) {
     constexpr int BM = 32 * M32;
     constexpr int A_ITERS = BM * 16 / 256;  // 16-byte pieces per lane per chunk
@@ -352,29 +353,34 @@ __global__ __launch_bounds__(256) void k_dense32(DenseArgs a) {
     };
 
     // prologue: the loads in flight at each step's start are, in issue order,
-    // weights c, activations c+1, weights c+1
-    Slot s0, s1;
+    // weights c, activations c+1, weights c+1 .. c+R-1 (chunk c+i in slot
+    // (c+i) mod R; indices past the end are clamped, redundant in-bounds loads)
+    static_assert(R == 2 || R == 3, "ring depth");
+    Slot sl[R];
 #pragma unroll
     for (int it = 0; it < A_ITERS; ++it) load_piece(it, 0);
-    load_B(0, s0);
+    load_B(0, sl[0]);
 #pragma unroll
     for (int it = 0; it < A_ITERS; ++it) store_piece(it, 0);
 #pragma unroll
     for (int it = 0; it < A_ITERS; ++it) load_piece(it, min(1, nch - 1));
-    load_B(min(1, nch - 1), s1);
+#pragma unroll
+    for (int q = 1; q < R; ++q) load_B(min(q, nch - 1), sl[q]);
     lds_barrier();
     auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
         compute(c, cur);
         __builtin_amdgcn_sched_barrier(0);
-        load_B(min(c + 2, nch - 1), cur);
+        load_B(min(c + R, nch - 1), cur);
         lds_barrier();
     };
     int c = 0;
-    for (; c + 2 <= nch; c += 2) {
-        step(c, s0);
-        step(c + 1, s1);
+    for (; c + R <= nch; c += R) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) step(c + q, sl[q]);
     }
-    if (c < nch) step(c, s0);
+#pragma unroll
+    for (int q = 0; q < R - 1; ++q)
+        if (c + q < nch) step(c + q, sl[q]);
 
 #pragma unroll
     for (int mb = 0; mb < M32; ++mb) {
@@ -507,22 +513,25 @@ int run_dense(int epi, const uint16_t* x, const uint16_t* w0, const uint16_t* w1
         return moe::launch_status(what);
     }
     if (M >= kDense32MinM) {
-        // 32x32 tiles of 128 rows (the weights, read from L2 once per row tile,
-        // dominate a tile's operand traffic: shorter tiles re-read them more
-        // often and measured slower even with twice the workgroups)
+        // 32x32 tiles of 128 rows, or 192 from kDense32TallM rows (the weights,
+        // read from L2 once per row tile, dominate a tile's operand traffic:
+        // taller tiles re-read them less often).  The 128-row tiles keep a
+        // 3-slot weight ring; the 192-row tiles' accumulators leave room for 2
+        // slots only (3 spill).  Measured on 2048 rows, 192-row tiles left too
+        // few workgroups (0.18 -> 0.22 ms); on 8192 rows they gained 10%.
         const int cols = sw ? 128 : 256;
         a.n_chunks = (N0 + cols - 1) / cols;
-        const int m32 = 4;
+        const int m32 = M >= kDense32TallM ? 6 : 4;
         a.tiles_m = (M + 32 * m32 - 1) / (32 * m32);
         a.n_logical = (long)a.tiles_m * a.n_chunks;
         a.per_xcd = moe::per_xcd(a.n_logical);
         const dim3 grid(8 * a.per_xcd), block(256);
-        if (m32 == 4) {
-            if (sw) hipLaunchKernelGGL((k_dense32<4, EPI_SWIGLU>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_dense32<4, EPI_LINEAR>), grid, block, 0, st, a);
+        if (m32 == 6) {
+            if (sw) hipLaunchKernelGGL((k_dense32<6, EPI_SWIGLU, 2>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_dense32<6, EPI_LINEAR, 2>), grid, block, 0, st, a);
         } else {
-            if (sw) hipLaunchKernelGGL((k_dense32<2, EPI_SWIGLU>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_dense32<2, EPI_LINEAR>), grid, block, 0, st, a);
+            if (sw) hipLaunchKernelGGL((k_dense32<4, EPI_SWIGLU, 3>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_dense32<4, EPI_LINEAR, 3>), grid, block, 0, st, a);
         }
         return moe::launch_status(what);
     }

@@ -442,6 +442,7 @@ def test_exact_linear_i8w_bitexact(m, M, N, K, seed):
     (700, 512, 256, False, 4),
     (300, 320, 384, True, 5),       # 32x32 tiles: ragged rows and a part-filled column chunk
     (4100, 4096, 128, True, 6),     # 32x32 tiles, many row tiles, ragged rows
+    (6200, 320, 384, True, 7),      # 192-row 32x32 tiles: ragged rows and a part-filled column chunk
 ])
 def test_linear_bf16(m, M, N, K, with_add, seed):
     say(f"linear M={M} N={N} K={K}")
@@ -460,7 +461,8 @@ def test_linear_bf16(m, M, N, K, with_add, seed):
 
 @pytest.mark.parametrize("M,H,I,seed", [(64, 256, 128, 0), (64, 7168, 2048, 1), (130, 512, 192, 2),
                                         (300, 256, 192, 3),     # 32x32 tiles, ragged rows and columns
-                                        (4096, 128, 2048, 4)])  # 32x32 tiles, many row tiles
+                                        (4096, 128, 2048, 4),   # 32x32 tiles, many row tiles
+                                        (6150, 256, 192, 5)])   # 192-row tiles, ragged rows and columns
 def test_dense_swiglu_and_silu_mul(m, M, H, I, seed):
     say(f"dense swiglu M={M} H={H} I={I}")
     g = np.random.default_rng(seed)
