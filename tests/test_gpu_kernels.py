@@ -443,6 +443,9 @@ def test_exact_linear_i8w_bitexact(m, M, N, K, seed):
     (300, 320, 384, True, 5),       # 32x32 tiles: ragged rows and a part-filled column chunk
     (4100, 4096, 128, True, 6),     # 32x32 tiles, many row tiles, ragged rows
     (6200, 320, 384, True, 7),      # 192-row 32x32 tiles: ragged rows and a part-filled column chunk
+    (255, 192, 256, False, 8),      # last row count of the 16x16 kernel
+    (256, 192, 256, True, 9),       # first row count of the 32x32 kernel (two whole 128-row tiles)
+    (6144, 64, 128, False, 10),     # first row count of the 192-row tiles (32 whole tiles)
 ])
 def test_linear_bf16(m, M, N, K, with_add, seed):
     say(f"linear M={M} N={N} K={K}")
