@@ -172,7 +172,7 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     from int4_routed_expert_moe_amd import synthetic
-    cfg0 = synthetic.CONFIGS[args.workload]
+    cfg0 = synthetic.WORKLOADS[args.workload]
     if args.traffic_from:
         if not args.calibrate_copy:
             sys.exit("--traffic-from needs --calibrate-copy MIB, the copy size of the counted run")

@@ -34,7 +34,7 @@ T_SH_G, T_SH_U, T_SH_D = 9, 10, 11
 T_LAT_DOWN, T_LAT_UP, T_GAIN = 12, 13, 14
 T_ZIPF_CAL, T_SAMPLE = 15, 16
 
-CONFIGS = {
+WORKLOADS = {
     1: dict(id=1, name="tiny", T=64, H=256, E=16, k=2, I=128, shared_I=128, L=None,
             mode="bf16", layer_seed=1, x_seed=1, rms_eps=1e-6, bias_range=0.1),
     2: dict(id=2, name="k25_decode", T=64, H=7168, E=384, k=8, I=2048, shared_I=2048, L=None,
@@ -154,7 +154,7 @@ def make_inputs(cfg_id: int, router_bias: np.ndarray | None = None, with_experts
 
     ``router_bias`` replaces the drawn correction bias (the skewed-routing
     workload requires its calibrated bias here)."""
-    cfg = dict(CONFIGS[cfg_id])
+    cfg = dict(WORKLOADS[cfg_id])
     if T is not None:
         cfg["T"] = T
     if cfg.get("zipf") and router_bias is None:

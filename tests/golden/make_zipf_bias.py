@@ -37,7 +37,7 @@ ITERS = 300
 
 
 def main():
-    cfg = dict(synthetic.CONFIGS[4])
+    cfg = dict(synthetic.WORKLOADS[4])
     E, k, T = cfg["E"], cfg["k"], cfg["T"]
     w, _ = synthetic.gen_router(cfg)
     x_cal = synthetic.calibration_x(cfg, T)

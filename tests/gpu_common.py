@@ -25,7 +25,7 @@ def inputs(cfg_id):
     """Workload cfg_id as numpy arrays; expert weights are shared by workloads of one layer."""
     if cfg_id in _inputs:
         return _inputs[cfg_id]
-    cfg = synthetic.CONFIGS[cfg_id]
+    cfg = synthetic.WORKLOADS[cfg_id]
     bias = None
     if cfg.get("zipf"):
         bias = synthetic.load_bias_file(os.path.join(GOLD, "zipf_bias_k25.txt"))

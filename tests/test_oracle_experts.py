@@ -164,9 +164,9 @@ def test_latent_and_layer_shapes_match_the_pages():
     lat = json.load(open(os.path.join(GOLD, "latent_up_params.json")))
     assert lat["in_features"] * lat["out_features"] == lat["params_per_layer"]
     assert lat["params_per_layer"] * lat["layers"] == lat["params_total"]
-    c5 = synthetic.CONFIGS[5]
+    c5 = synthetic.WORKLOADS[5]
     assert (c5["L"], c5["H"]) == (lat["in_features"], lat["out_features"])
     shp = json.load(open(os.path.join(GOLD, "k25_layer_shape.json")))
     for cid in (2, 3, 4, 5):
-        c = synthetic.CONFIGS[cid]
+        c = synthetic.WORKLOADS[cid]
         assert (c["E"], c["k"], c["H"]) == (shp["routed_experts"], shp["experts_per_token"], shp["hidden"])

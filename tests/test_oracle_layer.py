@@ -9,7 +9,7 @@ from int4_routed_expert_moe_amd import synthetic
 
 
 def _small_latent_inputs():
-    cfg = dict(synthetic.CONFIGS[1], id=99, name="tiny_latent", L=128, layer_seed=99, x_seed=99)
+    cfg = dict(synthetic.WORKLOADS[1], id=99, name="tiny_latent", L=128, layer_seed=99, x_seed=99)
     return {
         "cfg": cfg,
         "x": synthetic.gen_x(cfg),
@@ -73,7 +73,7 @@ def test_latent_wiring():
 
 
 def test_exact_mode_tiny_layer_consistency():
-    cfg = dict(synthetic.CONFIGS[1], id=98, mode="exact", shared_I=None)
+    cfg = dict(synthetic.WORKLOADS[1], id=98, mode="exact", shared_I=None)
     inp = {
         "cfg": cfg, "x": synthetic.gen_x(cfg), "router_w": synthetic.gen_router(cfg)[0],
         "router_b": synthetic.gen_router(cfg)[1], "experts": synthetic.gen_experts(cfg),
