@@ -116,10 +116,15 @@ int moe_route_grouped(const uint16_t* x, const uint16_t* w_router, const float* 
  *   offsets[e]  = sum_{e' < e} counts[e'],  offsets[E] = T*k
  *   sorted_slot = the slots ordered by expert, stable in f
  *   slot_pos[f] = position of f in sorted_slot (its inverse)
- * Requires every topk_idx value in [0, E).  Bit-exact and deterministic;
- * one workgroup, no host synchronisation. */
+ * Requires every topk_idx value in [0, E).  Bit-exact and deterministic; no
+ * host synchronisation.  Up to 16383 slots (T*k) one workgroup does it all
+ * and ws may be NULL; from 16384 slots the slots are cut into blocks of 1024
+ * and ws (device, 16-byte aligned, at least moe_permute_workspace_bytes(T, k,
+ * E) bytes, 0 below that size) holds per-block expert counts between three
+ * launches; the result is the same either way. */
+size_t moe_permute_workspace_bytes(int T, int k, int E);
 int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
-                int32_t* sorted_slot, int32_t* slot_pos, void* stream);
+                int32_t* sorted_slot, int32_t* slot_pos, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Exact-mode activation quantiser ("Kimi exact-generator adaptation", "The

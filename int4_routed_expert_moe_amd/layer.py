@@ -105,6 +105,7 @@ class MoELayer:
         staged = not exact and T >= self.STAGED_ACT_MIN_T
         w = {
             "route_ws": torch.empty(max(1, _m.moe_route_workspace_bytes(T, self.H, E)), dtype=torch.uint8, device=dev),
+            "perm_ws": torch.empty(max(1, _m.moe_permute_workspace_bytes(T, k, E)), dtype=torch.uint8, device=dev),
             "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
             "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
             "counts": torch.empty(E, dtype=torch.int32, device=dev),
@@ -185,7 +186,7 @@ class MoELayer:
             _m.moe_route_grouped(x, self.router_w, self.router_b, k, True, self.n_group, self.topk_group,
                                  self.routed_scale, w["topk_idx"], w["topk_w"], w["route_ws"])
         mark("moe_route")
-        _m.moe_permute(w["topk_idx"], E, w["counts"], w["offsets"], w["sorted_slot"], w["slot_pos"])
+        _m.moe_permute(w["topk_idx"], E, w["counts"], w["offsets"], w["sorted_slot"], w["slot_pos"], w["perm_ws"])
         mark("moe_permute")
         act = x
         if self.latent is not None:

@@ -72,10 +72,21 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.moe_route_workspace_bytes(4096, 7168, 384) == 4096 * 384 * 4  # logits
     # zero tokens is a no-op
     assert _status(lib, "moe_route", null, null, null, 0, 256, 16, 2, 1, null, null, null, ctypes.c_size_t(0), null) == 0
-    # permute: E too large, k > 16
-    assert _status(lib, "moe_permute", fake, 4, 2, 4096, fake, fake, fake, fake, null) == -2
-    assert _status(lib, "moe_permute", fake, 4, 17, 64, fake, fake, fake, fake, null) == -2
-    assert _status(lib, "moe_permute", fake, 4, 2, 64, null, fake, fake, fake, null) == -1
+    # permute: E too large, k > 16, null counts; from 16384 slots a workspace of per-block counts
+    z = ctypes.c_size_t(0)
+    assert _status(lib, "moe_permute", fake, 4, 2, 4096, fake, fake, fake, fake, null, z, null) == -2
+    assert _status(lib, "moe_permute", fake, 4, 17, 64, fake, fake, fake, fake, null, z, null) == -2
+    assert _status(lib, "moe_permute", fake, 4, 2, 64, null, fake, fake, fake, null, z, null) == -1
+    lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.moe_permute_workspace_bytes(64, 8, 384) == 0              # one workgroup
+    assert lib.moe_permute_workspace_bytes(2047, 8, 384) == 0            # 16376 slots
+    assert lib.moe_permute_workspace_bytes(2048, 8, 384) == 16 * 384 * 4  # 16 blocks of 1024 slots
+    assert lib.moe_permute_workspace_bytes(8192, 8, 384) == 64 * 384 * 4
+    assert lib.moe_permute_workspace_bytes(3001, 7, 5) == 21 * 5 * 4      # ragged last block
+    need = ctypes.c_size_t(16 * 384 * 4)
+    assert _status(lib, "moe_permute", fake, 2048, 8, 384, fake, fake, fake, fake, null, z, null) == -3
+    assert _status(lib, "moe_permute", fake, 2048, 8, 384, fake, fake, fake, fake, fake, ctypes.c_size_t(100), null) == -3
+    assert _status(lib, "moe_permute", fake, 2048, 8, 384, fake, fake, fake, fake, odd, need, null) == -1
     # grouped gemms: bad mode, unsupported widths, scales in the wrong mode, null pointers
     g = "moe_int4_grouped_swiglu"
     assert _status(lib, g, 7, fake, null, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1

@@ -136,8 +136,13 @@ def test_sigmoid_matches_oracle_on_a_sweep(m):
 
 
 # ---------------------------------------------------------------- permutation
-@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (64, 2, 16, 1), (64, 8, 384, 2), (8192, 8, 384, 3),
-                                        (1000, 16, 1024, 4), (77, 3, 5, 5)])
+@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (64, 2, 16, 1), (64, 8, 384, 2),
+                                        (8192, 8, 384, 3),     # blocks of 1024 slots
+                                        (1000, 16, 1024, 4),   # 16000 slots: largest one-workgroup case
+                                        (77, 3, 5, 5),
+                                        (2048, 8, 1024, 6),    # 16384 slots: first multi-block case, largest E
+                                        (3001, 7, 5, 7),       # multi-block, ragged last block, few experts
+                                        (16384, 1, 1, 8)])     # multi-block, one expert
 def test_permute_bitexact(m, T, k, E, seed):
     say(f"permute T={T} k={k} E={E}")
     g = np.random.default_rng(seed)
@@ -148,7 +153,8 @@ def test_permute_bitexact(m, T, k, E, seed):
     S = T * k
     d = {n: torch.empty(s, dtype=torch.int32, device="cuda") for n, s in
          (("counts", E), ("offsets", E + 1), ("ss", S), ("sp", S))}
-    m.moe_permute(torch.from_numpy(idx).cuda(), E, d["counts"], d["offsets"], d["ss"], d["sp"])
+    ws = torch.empty(max(1, m.moe_permute_workspace_bytes(T, k, E)), dtype=torch.uint8, device="cuda")
+    m.moe_permute(torch.from_numpy(idx).cuda(), E, d["counts"], d["offsets"], d["ss"], d["sp"], ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(d["counts"].cpu().numpy(), rc)
     np.testing.assert_array_equal(d["offsets"].cpu().numpy(), ro)
