@@ -452,6 +452,9 @@ def test_exact_linear_i8w_bitexact(m, M, N, K, seed):
     (255, 192, 256, False, 8),      # last row count of the 16x16 kernel
     (256, 192, 256, True, 9),       # first row count of the 32x32 kernel (two whole 128-row tiles)
     (6144, 64, 128, False, 10),     # first row count of the 192-row tiles (32 whole tiles)
+    (16, 512, 2048, False, 11),     # split K, 16-row tiles
+    (30, 320, 1024, True, 12),      # split K, 32-row tiles, ragged rows and columns
+    (50, 128, 2560, True, 13),      # split K into splits of 2 and 3 chunks
 ])
 def test_linear_bf16(m, M, N, K, with_add, seed):
     say(f"linear M={M} N={N} K={K}")
