@@ -111,7 +111,7 @@ def _counter_means(folder, counter):
                 continue
             name = r["Kernel_Name"]
             m = re.search(r"k_grouped(?:_skinny|_exact)?<(\d+), (\d+)", name)   # <mode, op, ...>
-            m32 = re.search(r"k_grouped32<(\d+),", name)                   # <op, m32>
+            m32 = re.search(r"k_grouped32(?:_dma)?<(\d+),", name)          # <op, m32>
             if m or m32:
                 op = m.group(2) if m else m32.group(1)
                 key = "moe_int4_grouped_swiglu" if op == "0" else "moe_int4_grouped_down"

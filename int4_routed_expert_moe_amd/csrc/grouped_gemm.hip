@@ -284,6 +284,29 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// One 16-byte buffer load per lane written straight to LDS: lane l's bytes go
+// to lds + 16 l (lds wave-uniform).  The builtin exists for the device pass
+// only; the host pass of this file compiles the kernels' launch stubs.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, uint32_t voffset,
+                                                  uint32_t soffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                             voffset, soffset, 0, 0);
+#else
+    (void)rsrc, (void)lds, (void)voffset, (void)soffset;
+#endif
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order).  Used where the compiler cannot see the wait:
+// LDS written by global-to-LDS loads, read by other waves after a barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Tiles of up to 16*MB rows on the 16x16x32 shape: bf16 tiles of 2, 4 or 6 row
 // blocks (mid-size batches) and every exact-mode tile (2 or 4 row blocks).  A
 // workgroup is 4 waves; each wave owns CB column blocks of 16 weight rows and
@@ -894,6 +917,217 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
     }
 }
 
+// k_grouped32 for activations already in the fp16 staging format, with the
+// activation tile staged by global-to-LDS buffer loads: the data goes straight
+// from memory into LDS, with no VGPRs, no LDS store instructions and no waits
+// in the product stream.  Such a load writes 16 bytes per lane at consecutive
+// LDS addresses (1 KB per wave instruction), so a tile row is 128 halves
+// unpadded and its 16-byte units are XOR-swizzled by the row's low four bits:
+// lane l of the instruction for rows R..R+3 writes physical unit l mod 16 of
+// row R + l/16 and fetches logical unit (l mod 16) ^ (row mod 16) for it; a
+// fragment read of 16 consecutive rows then touches every bank once.  Three
+// tile buffers: chunk c+2 is loaded while chunk c is multiplied, and a wave
+// waits for its own loads of chunk c+1 (issued a whole chunk earlier) before
+// the barrier that ends step c.  Same products and results as k_grouped32.
+template <int OP, int M32>
+__global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
+    constexpr int BM = 32 * M32;
+    constexpr bool GATEUP = OP == 0;
+    constexpr int A_ITERS = BM / 16;  // staging instructions per wave per chunk (4 rows each)
+    static_assert(A_ITERS * 4 * 4 == BM, "staging: 4 rows per wave instruction");
+
+    // three separate LDS objects, so that the compiler can tell a read of one
+    // buffer from the loads into another (it waits for those only on overlap)
+    __shared__ __attribute__((aligned(16))) _Float16 As0[BM][kKC];
+    __shared__ __attribute__((aligned(16))) _Float16 As1[BM][kKC];
+    __shared__ __attribute__((aligned(16))) _Float16 As2[BM][kKC];
+    __shared__ int32_t rowsrc[BM];
+    auto tile = [&](auto bufc) -> _Float16(&)[BM][kKC] {
+        if constexpr (decltype(bufc)::value == 0) return As0;
+        else if constexpr (decltype(bufc)::value == 1) return As1;
+        else return As2;
+    };
+
+    TileInfo ti;
+    int nc;
+    if (!locate_item(a.offsets, a.E, BM, a.n_chunks, ti, nc)) return;
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid >> 6;
+    const int c32 = lane & 31;
+    const int kb = lane >> 5;
+    const int K = a.K;
+    const int N = a.N;
+    const int nch = K / kKC;
+
+    if (tid < BM) {
+        int src = -1;
+        if (tid < ti.rows) src = GATEUP ? a.sorted_slot[ti.row0 + tid] / a.k : ti.row0 + tid;
+        rowsrc[tid] = src;
+    }
+
+    const int n0 = GATEUP ? (nc * 4 + wave) * 32 : (nc * 4 + wave) * 64;
+    const uint8_t* wf[2];
+    const uint16_t* sf[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+        const int n16 = (GATEUP ? n0 : n0 + 32 * cb) / 16 + (c32 >> 4);
+        const bool second = GATEUP && cb == 1;
+        const size_t f = frag_index(ti.e, n16, N, nch);
+        wf[cb] = (second ? a.w1 : a.w0) + f * kFragBytes + ((c32 & 15) + 16 * kb) * 16;
+        sf[cb] = (second ? a.s1 : a.s0) + f * kFragScales + 4 * (c32 & 15);
+    }
+    lds_barrier();  // rowsrc visible
+
+    // staging instruction it of this wave: tile rows R = A_ITERS*4*wave + 4*it .. R+3
+    // (rows past the tile take the tile's first row)
+    uint32_t aoff[A_ITERS];
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) {
+        const int row = A_ITERS * 4 * wave + 4 * it + (lane >> 4);
+        const int src = rowsrc[row];
+        const uint32_t unit = (uint32_t)((lane & 15) ^ (row & 15));
+        aoff[it] = ((uint32_t)(src >= 0 ? src : rowsrc[0]) * (uint32_t)K + unit * 8u) * 2u;
+    }
+    const __amdgpu_buffer_rsrc_t act_rsrc = buffer_rsrc(a.act, a.act_bytes);
+    auto dma_piece = [&](int it, int c, auto bufc) __attribute__((always_inline)) {
+        buffer_load_lds16(act_rsrc, &tile(bufc)[A_ITERS * 4 * wave + 4 * it][0], aoff[it], (uint32_t)c * (kKC * 2));
+    };
+
+    struct Slot {
+        u32x4_t B[2][2];
+        u32x2_t S[2];
+    };
+    auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            sl.B[cb][0] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
+            sl.B[cb][1] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes + 512);
+            sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
+        }
+    };
+
+    f32x16_t acc[M32][2];
+#pragma unroll
+    for (int mb = 0; mb < M32; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][cb][i] = 0.0f;
+
+    auto dequant_k = [&](const Slot& sl, int st, half8_t (&bf)[2]) __attribute__((always_inline)) {
+        const int g = st >> 1;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            half2_t s2, c2;
+            scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
+            bf[cb] = dequant8(sl.B[cb][st & 1][g], s2, c2);
+        }
+    };
+    // One stream of 8*NACT (K step, row block) products reading tile buffer BUF;
+    // the staging loads of chunk c+2 into buffer (BUF+2) mod 3 are spread over
+    // its first half (the barrier that ends the step waits for all of this wave's
+    // staging loads: the LDS release there covers them).
+    auto compute = [&](auto nact, auto bufc, int c, const Slot& sl) __attribute__((always_inline)) {
+        constexpr int NACT = decltype(nact)::value;
+        constexpr int BUF = decltype(bufc)::value;
+        constexpr int NS = 8 * NACT;
+        constexpr int PF = 4;
+        const int swz = c32 & 15;
+        auto frag = [&](int p) __attribute__((always_inline)) {
+            const int unit = (2 * (p / NACT) + kb) ^ swz;
+            return *reinterpret_cast<const half8_t*>(&tile(bufc)[32 * (p % NACT) + c32][8 * unit]);
+        };
+        half8_t afr[NS];
+#pragma unroll
+        for (int q = 0; q < PF; ++q) afr[q] = frag(q);
+        half8_t bfa[2], bfb[2];
+        dequant_k(sl, 0, bfa);
+        const int cs = min(c + 2, nch - 1);
+        static_for<NS>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int p = decltype(pc)::value;
+            constexpr int st = p / NACT;
+            constexpr int mb = p % NACT;
+            if constexpr (p + PF < NS) afr[p + PF] = frag(p + PF);
+            static_for<A_ITERS>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i * NS / (2 * A_ITERS) == p)
+                    dma_piece(i, cs, std::integral_constant<int, (BUF + 2) % 3>{});
+            });
+            if constexpr (mb == 0 && st < 7) dequant_k(sl, st + 1, (st & 1) ? bfa : bfb);
+            half8_t(&cur)[2] = (st & 1) ? bfb : bfa;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[p], cur[cb], acc[mb][cb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0x0002);
+        });
+    };
+
+    // Loads issued, in order, in the steady state: ... staging c+1, weights c+2 |
+    // step c: staging c+2 (A_ITERS), weights c+3 (6) | wait: staging c+1 done
+    // when at most 6 + A_ITERS + 6 younger loads are outstanding (the release
+    // before the barrier then also waits for staging c+2, issued in the first
+    // half of the step).  The prologue issues staging 0, weights 0, weights 1,
+    // staging 1, weights 2 and waits for staging 0 the same way (6 + 6 +
+    // A_ITERS + 6 younger).
+    auto main_loop = [&](auto nact) __attribute__((always_inline)) {
+        Slot s0, s1, s2;
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it) dma_piece(it, 0, std::integral_constant<int, 0>{});
+        load_B(0, s0);
+        load_B(min(1, nch - 1), s1);
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it) dma_piece(it, min(1, nch - 1), std::integral_constant<int, 1>{});
+        load_B(min(2, nch - 1), s2);
+        wait_vmcnt<18 + A_ITERS>();
+        lds_barrier();
+        auto step = [&](auto bufc, int c, Slot& cur) __attribute__((always_inline)) {
+            compute(nact, bufc, c, cur);
+            __builtin_amdgcn_sched_barrier(0);
+            load_B(min(c + 3, nch - 1), cur);
+            wait_vmcnt<12 + A_ITERS>();
+            lds_barrier();
+        };
+        int c = 0;
+        for (; c + 3 <= nch; c += 3) {
+            step(std::integral_constant<int, 0>{}, c, s0);
+            step(std::integral_constant<int, 1>{}, c + 1, s1);
+            step(std::integral_constant<int, 2>{}, c + 2, s2);
+        }
+        if (c < nch) step(std::integral_constant<int, 0>{}, c, s0);
+        if (c + 1 < nch) step(std::integral_constant<int, 1>{}, c + 1, s1);
+    };
+    const int nact = (ti.rows + 31) >> 5;
+    static_for<M32>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int n = decltype(ic)::value + 1;
+        if (nact == n) main_loop(std::integral_constant<int, n>{});
+    });
+    wait_vmcnt<0>();  // the trailing (redundant) staging loads land before the wave ends
+
+#pragma unroll
+    for (int mb = 0; mb < M32; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
+            if (rl >= ti.rows) continue;
+            const size_t orow = (size_t)(ti.row0 + rl);
+            if (GATEUP) {
+                const uint32_t gb = f32_to_bf16_bits(acc[mb][0][i]);
+                const uint32_t ub = f32_to_bf16_bits(acc[mb][1][i]);
+                const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
+                const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
+                store_h<true>(a.out, orow * N, n0 + c32, hb);
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    static_cast<uint16_t*>(a.out)[orow * N + n0 + 32 * cb + c32] =
+                        (uint16_t)f32_to_bf16_bits(acc[mb][cb][i]);
+            }
+        }
+    }
+}
+
 // Tiles of at most 16 rows (decode): the weights dominate the bytes, so each
 // wave streams its 64 weight rows (4 fragments per chunk) independently, with
 // no workgroup barrier and no LDS.  Bytes in flight set the speed here: the
@@ -1151,8 +1385,11 @@ template <int MODE, int OP, int M32>
 void launch_tiles32(GroupedArgs a, int S, hipStream_t st) {
     a.n_chunks = OP == 0 ? a.N / 128 : a.N / 256;
     const long tiles = ((long)S + (long)a.E * (32 * M32 - 1)) / (32 * M32) + 1;
-    hipLaunchKernelGGL((k_grouped32<OP, M32, MODE == MOE_MODE_BF16_F16P>), dim3(8 * moe::per_xcd(tiles * a.n_chunks)),
-                       dim3(256), 0, st, a);
+    const dim3 grid(8 * moe::per_xcd(tiles * a.n_chunks));
+    if constexpr (MODE == MOE_MODE_BF16_F16P)
+        hipLaunchKernelGGL((k_grouped32_dma<OP, M32>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_grouped32<OP, M32, false>), grid, dim3(256), 0, st, a);
 }
 
 template <int MODE, int OP>
