@@ -1187,8 +1187,12 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
     auto load = [&](int c, Slot& sl) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            sl.B[cb] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
-            sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
+            // weights and scales are read once per launch: non-temporal loads keep
+            // them from displacing the activation rows in the caches (measured 4-5%
+            // faster for gate/up and about 2% for down, which then fetches 10% more
+            // bytes than the plain loads did)
+            sl.B[cb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes));
+            sl.S[cb] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales));
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
