@@ -162,6 +162,26 @@ def test_permute_bitexact(m, T, k, E, seed):
     np.testing.assert_array_equal(d["sp"].cpu().numpy(), rp)
 
 
+def test_permute_bitexact_skewed(m):
+    """Multi-block path with one expert holding most slots and most experts empty."""
+    T, k, E = 2600, 8, 256
+    say(f"permute skewed T={T} k={k} E={E}")
+    g = np.random.default_rng(11)
+    idx = np.where(g.random((T, k)) < 0.9, 7, g.integers(0, 20, (T, k))).astype(np.int32)
+    rc, ro, rs, rp = oracle.permute(idx, E)
+    S = T * k
+    d = {n: torch.empty(s, dtype=torch.int32, device="cuda") for n, s in
+         (("counts", E), ("offsets", E + 1), ("ss", S), ("sp", S))}
+    ws = torch.empty(max(1, m.moe_permute_workspace_bytes(T, k, E)), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 1  # the multi-block path
+    m.moe_permute(torch.from_numpy(idx).cuda(), E, d["counts"], d["offsets"], d["ss"], d["sp"], ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d["counts"].cpu().numpy(), rc)
+    np.testing.assert_array_equal(d["offsets"].cpu().numpy(), ro)
+    np.testing.assert_array_equal(d["ss"].cpu().numpy(), rs)
+    np.testing.assert_array_equal(d["sp"].cpu().numpy(), rp)
+
+
 # ---------------------------------------------------------------- exact-mode primitives
 @pytest.mark.parametrize("M,K,seed", [(1, 32, 0), (37, 256, 1), (64, 7168, 2)])
 def test_quant_act_bitexact(m, M, K, seed):
@@ -276,6 +296,7 @@ def _routing(g, T, E, k, skew=False):
     (700, 512, 256, 6, 2, False, 3),     # largest tile height
     (280, 256, 128, 8, 2, False, 4),     # 6-block tiles
     (400, 512, 256, 8, 2, True, 5),      # 8-block tiles, skewed
+    (700, 256, 128, 6, 2, False, 6),     # 32x32 tiles over 2 K chunks (gate/up) and 1 (down)
 ])
 def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     say(f"grouped bf16 T={T} H={H} I={I} E={E} k={k}")
