@@ -33,8 +33,8 @@ INT8_PEAK_TOPS = 5000.0
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5],
                     help="1 tiny, 2 K2.5 decode (default), 3 K2.5 prefill, 4 exact-mode Zipf, 5 K3 latent")
     ap.add_argument("--kernel-steps", type=int, default=10, help="forwards timed per kernel with events")
