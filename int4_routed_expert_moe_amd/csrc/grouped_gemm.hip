@@ -961,12 +961,6 @@ __global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
     const int N = a.N;
     const int nch = K / kKC;
 
-    if (tid < BM) {
-        int src = -1;
-        if (tid < ti.rows) src = GATEUP ? a.sorted_slot[ti.row0 + tid] / a.k : ti.row0 + tid;
-        rowsrc[tid] = src;
-    }
-
     const int n0 = GATEUP ? (nc * 4 + wave) * 32 : (nc * 4 + wave) * 64;
     const uint8_t* wf[2];
     const uint16_t* sf[2];
@@ -977,6 +971,31 @@ __global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
         const size_t f = frag_index(ti.e, n16, N, nch);
         wf[cb] = (second ? a.w1 : a.w0) + f * kFragBytes + ((c32 & 15) + 16 * kb) * 16;
         sf[cb] = (second ? a.s1 : a.s0) + f * kFragScales + 4 * (c32 & 15);
+    }
+
+    struct Slot {
+        u32x4_t B[2][2];
+        u32x2_t S[2];
+    };
+    auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            sl.B[cb][0] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
+            sl.B[cb][1] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes + 512);
+            sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
+        }
+    };
+    // the first three weight chunks depend only on the tile's expert: they go out
+    // before the activation rows are gathered, so the two latencies overlap
+    Slot s0, s1, s2;
+    load_B(0, s0);
+    load_B(min(1, nch - 1), s1);
+    load_B(min(2, nch - 1), s2);
+
+    if (tid < BM) {
+        int src = -1;
+        if (tid < ti.rows) src = GATEUP ? a.sorted_slot[ti.row0 + tid] / a.k : ti.row0 + tid;
+        rowsrc[tid] = src;
     }
     lds_barrier();  // rowsrc visible
 
@@ -993,19 +1012,6 @@ __global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
     const __amdgpu_buffer_rsrc_t act_rsrc = buffer_rsrc(a.act, a.act_bytes);
     auto dma_piece = [&](int it, int c, auto bufc) __attribute__((always_inline)) {
         buffer_load_lds16(act_rsrc, &tile(bufc)[A_ITERS * 4 * wave + 4 * it][0], aoff[it], (uint32_t)c * (kKC * 2));
-    };
-
-    struct Slot {
-        u32x4_t B[2][2];
-        u32x2_t S[2];
-    };
-    auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            sl.B[cb][0] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes);
-            sl.B[cb][1] = *reinterpret_cast<const u32x4_t*>(wf[cb] + (size_t)c * kFragBytes + 512);
-            sl.S[cb] = *reinterpret_cast<const u32x2_t*>(sf[cb] + (size_t)c * kFragScales);
-        }
     };
 
     f32x16_t acc[M32][2];
@@ -1064,29 +1070,23 @@ __global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
         });
     };
 
-    // Loads issued, in order, in the steady state: ... staging c+1, weights c+2 |
-    // step c: staging c+2 (A_ITERS), weights c+3 (6) | wait: staging c+1 done
-    // when at most 6 + A_ITERS + 6 younger loads are outstanding (the release
-    // before the barrier then also waits for staging c+2, issued in the first
-    // half of the step).  The prologue issues staging 0, weights 0, weights 1,
-    // staging 1, weights 2 and waits for staging 0 the same way (6 + 6 +
-    // A_ITERS + 6 younger).
+    // Loads issued, in order: weights 0, 1, 2 (above), staging 0, staging 1 |
+    // step c: staging c+2 (A_ITERS pieces, first half of the step), weights c+3
+    // (6) | wait: staging c+1 done when at most 6 + A_ITERS younger loads are
+    // outstanding (the release before the barrier then also waits for staging
+    // c+2).  The prologue waits for staging 0 with staging 1 still in flight.
     auto main_loop = [&](auto nact) __attribute__((always_inline)) {
-        Slot s0, s1, s2;
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) dma_piece(it, 0, std::integral_constant<int, 0>{});
-        load_B(0, s0);
-        load_B(min(1, nch - 1), s1);
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) dma_piece(it, min(1, nch - 1), std::integral_constant<int, 1>{});
-        load_B(min(2, nch - 1), s2);
-        wait_vmcnt<18 + A_ITERS>();
+        wait_vmcnt<A_ITERS>();
         lds_barrier();
         auto step = [&](auto bufc, int c, Slot& cur) __attribute__((always_inline)) {
             compute(nact, bufc, c, cur);
             __builtin_amdgcn_sched_barrier(0);
             load_B(min(c + 3, nch - 1), cur);
-            wait_vmcnt<12 + A_ITERS>();
+            wait_vmcnt<6 + A_ITERS>();
             lds_barrier();
         };
         int c = 0;
