@@ -43,7 +43,7 @@ class MoELayer:
     `experts` holds the routed weights in the checkpoint layout; they are
     permuted once into the fragment layout here."""
 
-    SIDE_STREAM_MIN_T = 1024  # tokens from which the shared expert runs on its own stream
+    SIDE_STREAM_MIN_T = 64  # tokens from which the shared expert runs on its own stream
     # tokens from which the bf16 expert input is converted once to the fp16 staging
     # format (instead of by every tile of the grouped GEMMs)
     STAGED_ACT_MIN_T = 256
@@ -148,8 +148,9 @@ class MoELayer:
         The shared expert depends only on x, so for batches of at least
         ``SIDE_STREAM_MIN_T`` tokens it runs on a second stream, overlapping the
         router, the permutation and the routed GEMMs; the combine (or the latent
-        up-projection) waits for it.  (At decode sizes it would take CUs from the
-        HBM-bound routed GEMMs instead, measured slower.)  The side stream first
+        up-projection) waits for it.  (At 64 tokens this measured 1% faster once the
+        decode kernel's weight loads were non-temporal, slower before; smaller
+        batches keep one stream.)  The side stream first
         waits for an event recorded on the current stream, which orders it after
         x and after the previous forward's use of its buffers.
         ``marks``: when a list is given, every call runs on the current stream and
