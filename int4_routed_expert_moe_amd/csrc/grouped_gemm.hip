@@ -1354,10 +1354,10 @@ __global__ __launch_bounds__(256) void k_act_f16p(const u32x4_t* __restrict__ x,
     if (i < blocks) out[i] = bf16x8_to_f16_perm(x[i]);
 }
 
-// chunk slots of the decode kernel (D-1 chunks in flight): 3 slots keep the
-// kernel at about 150 VGPRs, three waves per SIMD; with the non-temporal weight
-// loads that measured 4-6% faster than 4 slots at two waves per SIMD
-constexpr int kSkinnyDepth = 3;
+// chunk slots of the decode kernel (D-1 chunks in flight): with the
+// non-temporal weight loads, more waves per SIMD beat a deeper ring per wave
+// (measured: 4 slots, two waves per SIMD < 3 slots, three < 2 slots)
+constexpr int kSkinnyDepth = 2;
 constexpr int kSkinnyDepthExact = 3;  // exact mode carries the activation scales too
 
 // Rows per tile: the smallest tile that holds an average expert segment with
