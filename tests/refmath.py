@@ -1,6 +1,9 @@
 """Test-side numerics used to pin the oracle: library routines (torch's bf16
 conversion, numpy's fp64 matmul and stable sorts) and a round-to-odd
 binary64 -> binary32 step, written independently of the oracle's code."""
+import math
+from fractions import Fraction
+
 import numpy as np
 import torch
 
@@ -60,3 +63,34 @@ def pack_int4_np(q):
 def silu64(z):
     z = np.asarray(z, dtype=np.float64)
     return z / (1.0 + np.exp(-z))
+
+
+def rn32(fr) -> float:
+    """The binary32 value nearest to a rational (normal range, or zero), ties to
+    even: the IEEE round-to-nearest of one exact result."""
+    fr = Fraction(fr)
+    if fr == 0:
+        return 0.0
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(float(a)))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    scaled = a / Fraction(2) ** (e - 23)
+    fl = math.floor(scaled)
+    rem = scaled - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return float(sign * fl * Fraction(2) ** (e - 23))
+
+
+def rint_half_even(fr) -> int:
+    """Round a rational to the nearest integer, ties to even."""
+    fr = Fraction(fr)
+    fl = math.floor(fr)
+    rem = fr - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return int(fl)

@@ -15,21 +15,7 @@ from tests import refmath
 getcontext().prec = 80
 
 
-def _rn32(fr: Fraction) -> float:
-    """Correctly rounded binary32 value of a rational (normal range), ties to even."""
-    sign = -1 if fr < 0 else 1
-    a = abs(fr)
-    e = math.floor(math.log2(float(a)))
-    while Fraction(2) ** e > a:
-        e -= 1
-    while Fraction(2) ** (e + 1) <= a:
-        e += 1
-    scaled = a / Fraction(2) ** (e - 23)
-    fl = math.floor(scaled)
-    rem = scaled - fl
-    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
-        fl += 1
-    return float(sign * fl * Fraction(2) ** (e - 23))
+_rn32 = refmath.rn32
 
 
 LN2 = Fraction(Decimal("0.69314718055994530941723212145817656807550013436025525412068000949339362"))
@@ -112,3 +98,58 @@ def test_f64_to_bf16_rounds_once():
     assert oracle.f64_to_bf16(v) == 0x3F81
     assert oracle.f64_to_bf16(1.0 + 2.0 ** -8) == 0x3F80  # tie -> even
     assert oracle.f64_to_bf16(1.0 + 3 * 2.0 ** -8) == 0x3F82  # tie -> even (up)
+
+
+# ---------------------------------------------------------------- exp_ref, step by step
+# The pinned definition of e^t (Cody & Waite 1980 reduction, degree-7 Taylor
+# polynomial by Horner's rule with fused multiply-adds, scaling by 2^n), emulated
+# here with exact rationals: each fp32 operation is its exact result rounded once
+# (an fma rounds a*b + c once), constants are the nearest binary32 values of the
+# mathematical constants.  A different polynomial degree, Horner order, a missing
+# low part of ln 2 or an unfused step changes some of these bits.
+
+def _emul_exp(t: float) -> float:
+    F = Fraction
+    log2e, ln2_hi = F(_rn32(LOG2E)), F(_rn32(LN2))
+    ln2_lo = F(_rn32(LN2 - ln2_hi))
+    c = [F(_rn32(F(1, math.factorial(m)))) for m in range(8)]
+    t = F(t)
+    n = refmath.rint_half_even(F(_rn32(t * log2e)))
+    r = F(_rn32(-n * ln2_hi + t))
+    r = F(_rn32(-n * ln2_lo + r))
+    p = c[7]
+    for m in range(6, -1, -1):
+        p = F(_rn32(p * r + c[m]))
+    return float(p * F(2) ** n)   # exact: the result stays in the normal range for |t| <= 80
+
+
+def _emul_sigmoid(z: float) -> float:
+    zc = min(max(z, -80.0), 80.0)
+    e = Fraction(_emul_exp(-zc))
+    return _rn32(Fraction(1) / Fraction(_rn32(1 + e)))
+
+
+def _exp_points():
+    g = np.random.default_rng(7)
+    pts = np.concatenate([
+        g.uniform(-80, 80, 160), g.uniform(-1, 1, 60), g.uniform(-1e-3, 1e-3, 20),
+        np.array([0.0, 0.5, -0.5, 0.3465736, 0.3465737, 1.0, -1.0, 80.0, -80.0, 79.99, 44.3614, -44.3614]),
+    ]).astype(np.float32)
+    return pts
+
+
+def test_exp_ref_matches_step_by_step_emulation():
+    t = _exp_points()
+    got = oracle.exp_ref_n(t)
+    ref = np.array([_emul_exp(float(v)) for v in t], dtype=np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_sigmoid_and_silu_match_step_by_step_emulation():
+    z = np.concatenate([_exp_points(), np.array([-90.0, 95.0, -80.5], np.float32)]).astype(np.float32)
+    s = oracle.sigmoid_ref_n(z)
+    ref = np.array([_emul_sigmoid(float(v)) for v in z], dtype=np.float32)
+    np.testing.assert_array_equal(s.view(np.uint32), ref.view(np.uint32))
+    silu = oracle.silu_ref_n(z)
+    ref_silu = np.array([_rn32(Fraction(float(v)) * Fraction(float(r))) for v, r in zip(z, ref)], dtype=np.float32)
+    np.testing.assert_array_equal(silu.view(np.uint32), ref_silu.view(np.uint32))

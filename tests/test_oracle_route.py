@@ -48,26 +48,6 @@ def test_logits_within_two_level_fp32_bound():
     assert np.all(np.abs(l - exact) <= bound)
 
 
-def test_logits_follow_the_two_level_order():
-    """A block whose sum cancels to zero exactly, then a small term: with a single
-    running sum the small term would be absorbed by the large partial sums; with
-    block sums it survives exactly."""
-    H, E = 128, 1
-    x = np.zeros((1, H), np.uint16)
-    w = np.zeros((E, H), np.uint16)
-    big, small = 2.0 ** 30, 1.0
-    vals = np.zeros(H, np.float32)
-    vals[0], vals[1], vals[64] = big, -big, small
-    x[0] = refmath.bf16_from_f32(vals)
-    w[0] = refmath.bf16_from_f32(np.ones(H, np.float32))
-    assert oracle.router_logits(x, w)[0, 0] == 1.0
-    # order inside a block is ascending: (big + small) - big loses the small term
-    vals2 = np.zeros(H, np.float32)
-    vals2[0], vals2[1], vals2[2] = big, small, -big
-    x[0] = refmath.bf16_from_f32(vals2)
-    assert oracle.router_logits(x, w)[0, 0] == 0.0
-
-
 def test_selection_is_stable_sort_of_biased_scores():
     T, H, E, k = 64, 256, 16, 4
     x, w, b = _rand_router(T, H, E, 2)
