@@ -126,6 +126,21 @@ size_t moe_permute_workspace_bytes(int T, int k, int E);
 int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
                 int32_t* sorted_slot, int32_t* slot_pos, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid allocation): the same
+ * arguments and results without the workspace.  From 16384 slots the
+ * per-block expert counts live in a fixed 1 MiB device array inside the
+ * library (one copy per GPU, held until the process ends), so the call
+ * supports ceil(T*k / 1024) * E <= 262144 there (at E = 384: up to 696,320
+ * slots) and returns MOE_ERR_UNSUPPORTED beyond it.  Every count entry is
+ * written before it is read, so nothing carries over from an earlier call.
+ * All calls on one GPU share that array: calls that overlap in time on one
+ * GPU (other streams, other host threads) race and must be serialised by the
+ * caller.  Allocates nothing; the first call on a device looks up the array's
+ * address for that device. */
+int moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_slot, int32_t* slot_pos, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Exact-mode activation quantiser ("Kimi exact-generator adaptation", "The
  * proposed substitution": ExactLinear with group size 32 and an activation

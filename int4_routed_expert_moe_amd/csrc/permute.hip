@@ -20,7 +20,16 @@
 //      first position per expert (one workgroup; blocks in order per expert);
 //   3. k_perm_block_scatter: per block, 4 waves with the single-workgroup
 //      scheme inside the block, starting from the block's first positions.
+#include <mutex>
+
 #include "moe_common.h"
+
+// Per-block count buffer of moe_permute_noalloc: a fixed device array (every
+// GPU the library runs on holds its own copy until the process ends).  Host
+// code reaches it only through the address hipGetSymbolAddress returns for
+// the current device; the array's name on the host is not a device address.
+constexpr long kNoAllocHistInts = 1L << 18;  // 1 MiB: blocks x E <= 262144
+static __device__ __align__(256) int32_t scratch[kNoAllocHistInts];
 
 namespace {
 
@@ -199,6 +208,61 @@ __global__ __launch_bounds__(256) void k_perm_block_scatter(const int32_t* __res
 
 long perm_blocks(long S) { return S >= kPermBlocksMinS ? (S + kPermBlock - 1) / kPermBlock : 0; }
 
+// Host-side checks shared by both permutation entry points.
+int check_permute(const char* what, const int32_t* topk_idx, int T, int k, int E, const int32_t* counts,
+                  const int32_t* offsets, const int32_t* sorted_slot, const int32_t* slot_pos) {
+    using namespace moe;
+    if (T < 0 || k <= 0 || E <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad sizes T=%d k=%d E=%d", what, T, k, E);
+    if (E > kPermMaxE || k > 16 || (long)T * k >= (1L << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d k=%d T=%d outside limits", what, E, k, T);
+    if (!counts || !offsets) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    if (T > 0 && (!topk_idx || !sorted_slot || !slot_pos)) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    return MOE_OK;
+}
+
+// The launches of both entry points; hist is the per-block count buffer
+// (unused below kPermBlocksMinS slots).
+int launch_permute(const char* what, const int32_t* topk_idx, int S, int E, int32_t* counts, int32_t* offsets,
+                   int32_t* sorted_slot, int32_t* slot_pos, int32_t* hist, hipStream_t st) {
+    using namespace moe;
+    const long nb = perm_blocks(S);
+    if (nb == 0) {
+        hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, st, topk_idx, S, E, counts, offsets, sorted_slot,
+                           slot_pos);
+        return launch_status(what);
+    }
+    hipLaunchKernelGGL(k_perm_block_counts, dim3((unsigned)nb), dim3(256), 0, st, topk_idx, S, E, hist);
+    if (int rc = launch_status(what)) return rc;
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, hist, (int)nb, S, E, counts, offsets);
+    if (int rc = launch_status(what)) return rc;
+    hipLaunchKernelGGL(k_perm_block_scatter, dim3((unsigned)nb), dim3(256), 0, st, topk_idx, S, E, hist, sorted_slot,
+                       slot_pos);
+    return launch_status(what);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_for_current_device(const char* what, int32_t** out) {
+    using namespace moe;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "%s: device %d", what, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ERR_LAUNCH, "%s: hipGetSymbolAddress: %s", what, hipGetErrorString(e));
+        g_scratch_dev[dev] = static_cast<int32_t*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" size_t moe_permute_workspace_bytes(int T, int k, int E) {
@@ -210,31 +274,32 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int k, int E, int32_t
                            int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* ws,
                            size_t ws_bytes, void* stream) {
     using namespace moe;
-    if (T < 0 || k <= 0 || E <= 0)
-        return fail(MOE_ERR_INVALID_ARG, "moe_permute: bad sizes T=%d k=%d E=%d", T, k, E);
-    if (E > kPermMaxE || k > 16 || (long)T * k >= (1L << 31))
-        return fail(MOE_ERR_UNSUPPORTED, "moe_permute: E=%d k=%d T=%d outside limits", E, k, T);
-    if (!counts || !offsets) return fail(MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
-    if (T > 0 && (!topk_idx || !sorted_slot || !slot_pos))
-        return fail(MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
+    const char* what = "moe_permute";
+    if (int rc = check_permute(what, topk_idx, T, k, E, counts, offsets, sorted_slot, slot_pos)) return rc;
+    const int S = T * k;
+    if (perm_blocks(S) > 0) {
+        const size_t need = moe_permute_workspace_bytes(T, k, E);
+        if (!ws || ws_bytes < need)
+            return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, ws_bytes, need);
+        if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", what);
+    }
+    return launch_permute(what, topk_idx, S, E, counts, offsets, sorted_slot, slot_pos, static_cast<int32_t*>(ws),
+                          as_stream(stream));
+}
+
+extern "C" int moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, int32_t* counts,
+                                   int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos, void* stream) {
+    using namespace moe;
+    const char* what = "moe_permute_noalloc";
+    if (int rc = check_permute(what, topk_idx, T, k, E, counts, offsets, sorted_slot, slot_pos)) return rc;
     const int S = T * k;
     const long nb = perm_blocks(S);
-    hipStream_t st = as_stream(stream);
-    if (nb == 0) {
-        hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, st, topk_idx, S, E, counts, offsets, sorted_slot,
-                           slot_pos);
-        return launch_status("moe_permute");
+    if (nb * (long)E > kNoAllocHistInts)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: %d slots over %d experts need %ld count entries, more than the fixed %ld",
+                    what, S, E, nb * (long)E, kNoAllocHistInts);
+    int32_t* hist = nullptr;
+    if (nb > 0) {
+        if (int rc = scratch_for_current_device(what, &hist)) return rc;
     }
-    const size_t need = moe_permute_workspace_bytes(T, k, E);
-    if (!ws || ws_bytes < need)
-        return fail(MOE_ERR_WORKSPACE, "moe_permute: workspace %zu < %zu bytes", ws_bytes, need);
-    if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARG, "moe_permute: workspace must be 16-byte aligned");
-    int32_t* hist = static_cast<int32_t*>(ws);
-    hipLaunchKernelGGL(k_perm_block_counts, dim3((unsigned)nb), dim3(256), 0, st, topk_idx, S, E, hist);
-    if (int rc = launch_status("moe_permute counts")) return rc;
-    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, hist, (int)nb, S, E, counts, offsets);
-    if (int rc = launch_status("moe_permute scan")) return rc;
-    hipLaunchKernelGGL(k_perm_block_scatter, dim3((unsigned)nb), dim3(256), 0, st, topk_idx, S, E, hist, sorted_slot,
-                       slot_pos);
-    return launch_status("moe_permute scatter");
+    return launch_permute(what, topk_idx, S, E, counts, offsets, sorted_slot, slot_pos, hist, as_stream(stream));
 }

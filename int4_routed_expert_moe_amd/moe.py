@@ -45,6 +45,7 @@ EXPORTS = {
     "moe_route_grouped": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _SZ, _P], _I),
     "moe_permute_workspace_bytes": ([_I, _I, _I], _SZ),
     "moe_permute": ([_P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "moe_permute_noalloc": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "moe_quant_act_int8": ([_P, _I, _I, _P, _P, _P], _I),
     "moe_int4_prepack": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
     "moe_act_f16p": ([_P, _I, _I, _P, _P], _I),
@@ -148,6 +149,18 @@ def moe_permute(topk_idx, E, counts, offsets, sorted_slot, slot_pos, ws=None):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("moe_permute", _lib.moe_permute(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets),
                                            _ptr(sorted_slot), _ptr(slot_pos), _ptr(ws), nbytes, _stream()))
+
+
+def moe_permute_noalloc(topk_idx, E, counts, offsets, sorted_slot, slot_pos):
+    """moe_permute without a workspace (the library's fixed device buffer holds the block counts)."""
+    T, k = topk_idx.shape
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    _need(counts, torch.int32, (E,), "counts")
+    _need(offsets, torch.int32, (E + 1,), "offsets")
+    _need(sorted_slot, torch.int32, (T * k,), "sorted_slot")
+    _need(slot_pos, torch.int32, (T * k,), "slot_pos")
+    _check("moe_permute_noalloc", _lib.moe_permute_noalloc(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets),
+                                                           _ptr(sorted_slot), _ptr(slot_pos), _stream()))
 
 
 def moe_quant_act_int8(x, q, s):

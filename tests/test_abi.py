@@ -83,6 +83,10 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert lib.moe_permute_workspace_bytes(2048, 8, 384) == 16 * 384 * 4  # 16 blocks of 1024 slots
     assert lib.moe_permute_workspace_bytes(8192, 8, 384) == 64 * 384 * 4
     assert lib.moe_permute_workspace_bytes(3001, 7, 5) == 21 * 5 * 4      # ragged last block
+    # the workspace-free permutation: its fixed buffer holds 256 blocks x 1024 experts of counts
+    assert _status(lib, "moe_permute_noalloc", fake, 32769, 8, 1024, fake, fake, fake, fake, null) == -2
+    assert b"262144" in lib.moe_last_error_detail()
+    assert _status(lib, "moe_permute_noalloc", fake, 4, 2, 64, null, fake, fake, fake, null) == -1
     need = ctypes.c_size_t(16 * 384 * 4)
     assert _status(lib, "moe_permute", fake, 2048, 8, 384, fake, fake, fake, fake, null, z, null) == -3
     assert _status(lib, "moe_permute", fake, 2048, 8, 384, fake, fake, fake, fake, fake, ctypes.c_size_t(100), null) == -3
