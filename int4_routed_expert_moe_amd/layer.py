@@ -3,7 +3,10 @@
 Kimi-K3 latent MoE page, Code (forward / moe_infer): the router sees the
 full-width hidden state; the latent variant projects it down before the
 routed experts and back up after an RMSNorm; the shared expert runs on the
-full-width input and is added last.  For the K2.5-shaped layer there is no
+full-width input and is added last.  The same Code's __init__ makes two steps
+optional, and the configuration carries them: ``renormalize`` (the selected
+weights divided by their sum, default on) and ``latent_norm`` (the RMSNorm
+before the up-projection, default on).  For the K2.5-shaped layer there is no
 latent step and the shared add happens inside the combine.
 
 Nothing here computes: the class owns device buffers (weights and a
@@ -63,6 +66,10 @@ class MoELayer:
         self.latent = latent
         self.E, self.k, self.H, self.I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
         self.Kin = cfg.get("L") or cfg["H"]  # width the routed experts see
+        # the K3 block's switches: renormalise the selected weights, RMSNorm the
+        # routed sum before the latent up-projection (both on by default)
+        self.renormalize = bool(cfg.get("renormalize", True))
+        self.latent_norm = bool(cfg.get("latent_norm", True))
         # group-limited routing (1 group, scale 1: plain sigmoid top-k)
         self.n_group = int(cfg.get("n_group", 1))
         self.topk_group = int(cfg.get("topk_group", 1))
@@ -182,9 +189,10 @@ class MoELayer:
         E, k, H, I, Kin = self.E, self.k, self.H, self.I, self.Kin
         ex = self.ex
         if self.n_group == 1 and self.routed_scale == 1.0:
-            _m.moe_route(x, self.router_w, self.router_b, k, True, w["topk_idx"], w["topk_w"], w["route_ws"])
+            _m.moe_route(x, self.router_w, self.router_b, k, self.renormalize, w["topk_idx"], w["topk_w"],
+                         w["route_ws"])
         else:
-            _m.moe_route_grouped(x, self.router_w, self.router_b, k, True, self.n_group, self.topk_group,
+            _m.moe_route_grouped(x, self.router_w, self.router_b, k, self.renormalize, self.n_group, self.topk_group,
                                  self.routed_scale, w["topk_idx"], w["topk_w"], w["route_ws"])
         mark("moe_route")
         _m.moe_permute(w["topk_idx"], E, w["counts"], w["offsets"], w["sorted_slot"], w["slot_pos"], w["perm_ws"])
@@ -235,9 +243,12 @@ class MoELayer:
         else:
             _m.moe_combine(self.mode, w["y"], w["slot_pos"], w["topk_w"], None, T, k, Kin, w["routed"])
             mark("moe_combine")
-            _m.moe_rmsnorm_bf16(w["routed"], self.latent["gain"], self.cfg["rms_eps"], w["normed"])
-            mark("moe_rmsnorm_bf16")
-            _m.moe_linear_bf16(w["normed"], self.latent["w_up"], shared_out, w["out"], w["dense_ws"])
+            up_in = w["routed"]
+            if self.latent_norm:
+                _m.moe_rmsnorm_bf16(w["routed"], self.latent["gain"], self.cfg["rms_eps"], w["normed"])
+                mark("moe_rmsnorm_bf16")
+                up_in = w["normed"]
+            _m.moe_linear_bf16(up_in, self.latent["w_up"], shared_out, w["out"], w["dense_ws"])
             mark("latent_up")
         return w["out"]
 

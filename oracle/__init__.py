@@ -481,7 +481,10 @@ def layer_tokens(inp, tokens, topk_idx=None, topk_w=None, want_intermediates=Fal
     ``inp`` is the dict produced by the seeded input generator (keys: cfg, x,
     router_w, router_b, experts{wg,sg,wu,su,wd,sd}, shared{wg,wu,wd} or None,
     latent{w_down,w_up,gain} or None).  Routing is computed here for the listed
-    tokens unless ``topk_idx``/``topk_w`` (full [T,k]) are given.  Returns
+    tokens unless ``topk_idx``/``topk_w`` (full [T,k]) are given.  The
+    configuration's ``renormalize`` and ``latent_norm`` switches ("Kimi-K3
+    latent MoE" page, Code: __init__'s moe_renormalize and latent_moe_use_norm)
+    default to on.  Returns
     out [n, H] (bf16 uint16 for the bf16 path, float32 for exact mode) and,
     when asked, the per-slot intermediates.
     """
@@ -489,12 +492,13 @@ def layer_tokens(inp, tokens, topk_idx=None, topk_w=None, want_intermediates=Fal
     k = cfg["k"]
     tokens = np.asarray(tokens, dtype=np.int64)
     x = inp["x"][tokens]
+    renorm = bool(cfg.get("renormalize", True))
     if topk_idx is None:
         if cfg.get("n_group", 1) != 1 or cfg.get("routed_scale", 1.0) != 1.0:
             idx, w = route_grouped(x, inp["router_w"], inp["router_b"], k, int(cfg.get("n_group", 1)),
-                                   int(cfg.get("topk_group", 1)), True, float(cfg.get("routed_scale", 1.0)))
+                                   int(cfg.get("topk_group", 1)), renorm, float(cfg.get("routed_scale", 1.0)))
         else:
-            idx, w = route(x, inp["router_w"], inp["router_b"], k, True)
+            idx, w = route(x, inp["router_w"], inp["router_b"], k, renorm)
     else:
         idx, w = topk_idx[tokens], topk_w[tokens]
     n = len(tokens)
@@ -531,7 +535,8 @@ def layer_tokens(inp, tokens, topk_idx=None, topk_w=None, want_intermediates=Fal
         if lat is None:
             out = combine_bf16(r["y"].reshape(n, k, Hr), w, sh_out)
         else:
-            nrm = rmsnorm_bf16(routed, lat["gain"], cfg["rms_eps"])
+            # the K3 block's latent_moe_use_norm switch (on unless the configuration turns it off)
+            nrm = rmsnorm_bf16(routed, lat["gain"], cfg["rms_eps"]) if cfg.get("latent_norm", True) else routed
             out = linear_bf16(nrm, lat["w_up"], add=sh_out)
             inter.update({"x_lat": xr, "normed": nrm})
             if want_intermediates:

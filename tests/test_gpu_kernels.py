@@ -357,6 +357,8 @@ def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     (45, 512, 256, 5, 3, False, 2),
     (280, 256, 128, 8, 2, False, 3),     # 6-block tiles
     (400, 512, 256, 8, 2, False, 4),     # 8-block tiles
+    (64, 1280, 640, 64, 8, False, 5),    # decode kernel: 8-row segments, 10 / 5 chunks through its ring
+    (48, 1024, 896, 32, 8, False, 6),    # decode kernel: 12-row segments, 8 / 7 chunks
 ])
 def test_grouped_exact_bitexact(m, T, H, I, E, k, skew, seed):
     say(f"grouped exact T={T} H={H} I={I} E={E} k={k}")
@@ -387,6 +389,62 @@ def test_grouped_exact_bitexact(m, T, H, I, E, k, skew, seed):
     torch.cuda.synchronize()
     ref_out = oracle.combine_f32(ref["y"][sp].reshape(T, k, H), w)
     np.testing.assert_array_equal(out.cpu().numpy(), ref_out)
+
+
+@pytest.mark.parametrize("mode_name", ["bf16", "exact"])
+def test_grouped_decode_kernel_odd_chunk_counts(m, mode_name):
+    """The decode kernel's weight ring over odd chunk counts: gate/up over 9 chunks of
+    128 (H = 1152), down over 5 (I = 640), with segments of about 8 rows."""
+    say(f"grouped decode kernel odd chunks mode={mode_name}")
+    g = np.random.default_rng(31)
+    T, E, k = 64, 64, 8
+    idx, _ = _routing(g, T, E, k)
+    counts, offsets, ss, sp = oracle.permute(idx, E)
+    off_d = torch.from_numpy(offsets).cuda()
+    S = T * k
+    # gate/up: H = 1152, I = 256
+    H, I = 1152, 256
+    W = _expert_set(g, E, H, I)
+    D = _dev_experts(W)
+    x = _rand_bf16(g, (T, H))
+    if mode_name == "bf16":
+        ref = oracle.experts_bf16(x[ss // k], idx.reshape(-1)[ss], W, want=("h",))
+        h = torch.empty((S, I), dtype=torch.bfloat16, device="cuda")
+        m.moe_int4_grouped_swiglu(m.MOE_MODE_BF16, bf16_dev(x), None, D["wg"], D["sg"], D["wu"], D["su"], off_d,
+                                  torch.from_numpy(ss).cuda(), T, k, E, H, I, h, None)
+        torch.cuda.synchronize()
+        assert_bf16_close(np_bf16(h), ref["h"], "h")
+    else:
+        qx, sx = oracle.quant_act_int8(x)
+        ref = oracle.experts_exact(qx[ss // k], sx[ss // k], idx.reshape(-1)[ss], W, want=("qh", "sh"))
+        qh = torch.empty((S, I), dtype=torch.int8, device="cuda")
+        sh = torch.empty((S, I // 32), dtype=torch.float32, device="cuda")
+        m.moe_int4_grouped_swiglu(m.MOE_MODE_EXACT_I8, torch.from_numpy(qx).cuda(), torch.from_numpy(sx).cuda(),
+                                  D["wg"], D["sg"], D["wu"], D["su"], off_d, torch.from_numpy(ss).cuda(), T, k, E,
+                                  H, I, qh, sh)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sh.cpu().numpy(), ref["sh"])
+        np.testing.assert_array_equal(qh.cpu().numpy(), ref["qh"])
+    # down: I = 640, H = 256, fed the oracle's h of a second expert set
+    H, I = 256, 640
+    W = _expert_set(g, E, H, I)
+    D = _dev_experts(W)
+    x = _rand_bf16(g, (T, H))
+    rows_e = idx.reshape(-1)[ss]
+    if mode_name == "bf16":
+        ref = oracle.experts_bf16(x[ss // k], rows_e, W, want=("h", "y"))
+        y = torch.empty((S, H), dtype=torch.bfloat16, device="cuda")
+        m.moe_int4_grouped_down(m.MOE_MODE_BF16, bf16_dev(ref["h"]), None, D["wd"], D["sd"], off_d, T, k, E, I, H, y)
+        torch.cuda.synchronize()
+        assert_bf16_close(np_bf16(y), ref["y"], "y")
+    else:
+        qx, sx = oracle.quant_act_int8(x)
+        ref = oracle.experts_exact(qx[ss // k], sx[ss // k], rows_e, W, want=("qh", "sh", "y"))
+        y = torch.empty((S, H), dtype=torch.float32, device="cuda")
+        m.moe_int4_grouped_down(m.MOE_MODE_EXACT_I8, torch.from_numpy(ref["qh"]).cuda(),
+                                torch.from_numpy(ref["sh"]).cuda(), D["wd"], D["sd"], off_d, T, k, E, I, H, y)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), ref["y"])
 
 
 @pytest.mark.parametrize("rows,K,seed", [(1, 8, 0), (37, 7168, 1), (300, 2048, 2)])

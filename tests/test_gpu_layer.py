@@ -170,3 +170,49 @@ def test_layer_exact16_on_skewed_routing():
     got = out.cpu().numpy()[toks]
     assert_f32_close(got, ref, "exact16 out", 1e-5)
     np.testing.assert_array_equal(got, ref)
+
+
+def _tiny_latent_inputs():
+    """A small latent block of the K3 shape family: hidden 512, latent 256, 16 experts,
+    top-2, intermediate 128, shared expert 128 (seeded like the workloads)."""
+    cfg = dict(synthetic.WORKLOADS[1], name="tiny_latent", H=512, L=256, layer_seed=11, x_seed=11)
+    w, b = synthetic.gen_router(cfg)
+    return {"cfg": cfg, "x": synthetic.gen_x(cfg), "router_w": w, "router_b": b,
+            "experts": synthetic.gen_experts(cfg), "shared": synthetic.gen_shared(cfg),
+            "latent": synthetic.gen_latent(cfg)}
+
+
+@pytest.mark.parametrize("renormalize,latent_norm,latent", [
+    (False, True, False),   # the tiny layer with raw sigmoid weights
+    (True, True, True),     # the latent block as the K3 page runs it
+    (True, False, True),    # the latent block without the RMSNorm
+    (False, False, True),   # both switches off
+])
+def test_layer_switches(renormalize, latent_norm, latent):
+    """The K3 block's switches ("Kimi-K3 latent MoE" page, Code: __init__'s
+    moe_renormalize and latent_moe_use_norm): routing bit-exact, every output
+    row within the bf16 bar of the oracle taking the same switches."""
+    from int4_routed_expert_moe_amd.layer import MoELayer
+    base = _tiny_latent_inputs() if latent else inputs(1)
+    inp = dict(base)
+    inp["cfg"] = dict(base["cfg"], renormalize=renormalize, latent_norm=latent_norm)
+    cfg = inp["cfg"]
+    L = MoELayer.from_numpy(inp, "cuda")
+    say(f"layer forward {cfg['name']} renormalize={renormalize} latent_norm={latent_norm}")
+    out = L.forward(bf16_dev(inp["x"]))
+    torch.cuda.synchronize()
+    ws = L.workspace(cfg["T"])
+    ridx, rw = oracle.route(inp["x"], inp["router_w"], inp["router_b"], cfg["k"], renormalize)
+    np.testing.assert_array_equal(ws["topk_idx"].cpu().numpy(), ridx)
+    np.testing.assert_array_equal(ws["topk_w"].cpu().numpy(), rw)
+    ref, inter = oracle.layer_tokens(inp, np.arange(cfg["T"]), want_intermediates=True)
+    if latent:
+        assert_bf16_close(np_bf16(ws["routed"]), inter["routed"], "routed")
+        terms = (inter["up"], inter["shared"])
+    else:
+        terms = (inter["routed"], inter["shared"])
+    assert_bf16_close(np_bf16(out), ref, "out", addends=terms)
+    # the switch changes the result
+    other = oracle.layer_tokens(dict(inp, cfg=dict(cfg, renormalize=True, latent_norm=True)), np.arange(4))
+    if not (renormalize and latent_norm):
+        assert (other != ref[:4]).any()
