@@ -48,6 +48,17 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of a run with "
                          "--calibrate-copy into profiles/<call>_<workload>_traffic.json")
+    ap.add_argument("--prefill-leg", dest="prefill_leg", action="store_true", default=None,
+                    help="after the headline workload, also time the same layer at prefill size (T=8192) and "
+                         "report it under 'prefill' (default: on for the default decode workload)")
+    ap.add_argument("--no-prefill-leg", dest="prefill_leg", action="store_false")
+    ap.add_argument("--no-hbm-probe", action="store_true", help="skip the streaming read and copy probes")
+    ap.add_argument("--json-out", metavar="PATH", help="also write the JSON line to PATH")
+    ap.add_argument("--stats-from", metavar="DIR",
+                    help="no run: summarise a rocprofv3 --kernel-trace --stats folder of a bench run (whose line "
+                         "--bench-json names) into profiles/moe_layer_<workload>_kernel_stats.md")
+    ap.add_argument("--bench-json", metavar="PATH", help="the --json-out file of the profiled run (for --stats-from)")
+    ap.add_argument("--profile-cmd", metavar="CMD", help="the profiled command, quoted in the summary (--stats-from)")
     return ap.parse_args()
 
 
@@ -165,6 +176,180 @@ def traffic_record(kernel, workload_name):
     return rec.get("bytes_per_launch")
 
 
+def roofline(cfg, counts, kernel_ms):
+    """The dominant call (largest event-timed duration among the layer's calls) against
+    its roofline, and the whole step against both peaks."""
+    work, layer_bytes, layer_flops, active = algorithmic_work(cfg, counts, cfg["shared_I"])
+    dom = max((n for n in kernel_ms if n in work), key=lambda n: kernel_ms[n])
+    b, f = work[dom]
+    dur_s = kernel_ms[dom] / 1e3
+    exact = cfg["mode"] == "exact"
+    if f / max(b, 1) < MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "hbm", "achieved": b / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    elif exact:
+        # exact mode is rated against the int8 matrix-core peak (its integer MACs), although
+        # the kernels run them as exact fp16 products
+        roof = {"bound": "mfma", "achieved": f / dur_s / 1e12, "peak": INT8_PEAK_TOPS, "unit": "TOP/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": f / dur_s / 1e12, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_record(dom, cfg["name"])
+    roof["kernel"] = dom
+    roof["kernel_ms"] = kernel_ms[dom]
+    roof["algorithmic_bytes"] = b
+    roof["algorithmic_flops"] = f
+    return roof, layer_bytes, layer_flops, active
+
+
+def time_layer(layer, x, steps, warmup, kernel_steps):
+    """ms per step over exactly `steps` timed forwards (after `warmup`), between two
+    synchronisations, and the per-call event durations of `kernel_steps` more forwards
+    (every call on the launch stream)."""
+    import torch
+    for _ in range(warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        layer.forward(x)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+    per = {}
+    for _ in range(kernel_steps):
+        marks = []
+        layer.forward(x, marks=marks)
+        torch.cuda.synchronize()
+        for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
+            per.setdefault(name, []).append(a.elapsed_time(b))
+    return ms_per_step, {n: float(np.mean(v)) for n, v in per.items()}, wall
+
+
+def hbm_probe():
+    """Context figures for the nominal 8 TB/s: a plain streaming read of 4 GiB
+    (libmoe_probe.so) and torch's device copy of 2 GiB (read + write bytes),
+    best of 5 each, timed with events."""
+    import ctypes
+
+    import torch
+    from int4_routed_expert_moe_amd import build as _b
+    lib = ctypes.CDLL(_b.PROBE_OUT)
+    lib.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.moe_probe_read.restype = ctypes.c_int
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)  # every 16-byte fold is 0, never 0xFFFFFFFF
+    blocks = 256 * 16
+    out = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best_read = 0.0
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        if lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr()), n, 0xFFFFFFFF, ctypes.c_void_p(out.data_ptr()), blocks,
+                              st) != 0:
+            raise RuntimeError("read probe launch failed")
+        b.record()
+        torch.cuda.synchronize()
+        best_read = max(best_read, n / (a.elapsed_time(b) / 1e3) / 1e9)
+    del buf
+    m = 2 << 30
+    src = torch.empty(m, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    best_copy = 0.0
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best_copy = max(best_copy, 2 * m / (a.elapsed_time(b) / 1e3) / 1e9)
+    del src, dst
+    return {"read_GBs": best_read, "copy_rw_GBs": best_copy, "read_bytes": n, "copy_bytes": m,
+            "read_frac_of_peak": best_read / HBM_PEAK_GBS,
+            "method": "best of 5: 16-byte grid-strided loads over 4 GiB (4096 workgroups); torch copy of 2 GiB"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def stats_summary(args):
+    """profiles/moe_layer_<workload>_kernel_stats.md from a rocprofv3 --kernel-trace --stats
+    folder of one bench run (without the prefill leg) and that run's --json-out line."""
+    import csv
+    import glob
+    import re
+    line = json.loads(open(args.bench_json).read().strip().splitlines()[-1])
+    run = line["run"]
+    n_fwd = run["warmup"] + run["steps"] + run["kernel_steps"]
+    stats_f = glob.glob(os.path.join(args.stats_from, "**", "*kernel_stats.csv"), recursive=True)
+    trace_f = glob.glob(os.path.join(args.stats_from, "**", "*kernel_trace.csv"), recursive=True)
+    if len(stats_f) != 1 or len(trace_f) != 1:
+        sys.exit(f"--stats-from: expected one kernel_stats.csv and one kernel_trace.csv under {args.stats_from}")
+    rows = list(csv.DictReader(open(stats_f[0])))
+    trace = sorted(csv.DictReader(open(trace_f[0])), key=lambda r: int(r["Start_Timestamp"]))
+    durs = {}
+    for r in trace:
+        durs.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def short(n):
+        n = n.replace("(anonymous namespace)::", "")
+        n = re.sub(r"^void ", "", n)
+        return re.sub(r"\(.*\)$", "", n)
+
+    def single_stream(name):
+        """Average of the kernel's dispatches in the last kernel_steps forwards (the
+        per-call event steps, every call alone on the launch stream)."""
+        d = durs.get(name, [])
+        if not d or len(d) % n_fwd:
+            return None
+        tail = d[-run["kernel_steps"] * (len(d) // n_fwd):]
+        return sum(tail) / len(tail)
+
+    cfg_name = line["config"]["workload"].split(":")[0]
+    ks = run["kernel_steps"]
+    out = [f"# Layer kernels, workload {cfg_name}", "",
+           "Command (on the MI355X, from the repository root), then the summary:", "", "```",
+           args.profile_cmd or "(not given)",
+           f"python3 bench.py --stats-from {args.stats_from} --bench-json {args.bench_json}", "```", "",
+           f"The run made {n_fwd} forwards: {run['warmup']} warmup, {run['steps']} timed (the shared expert on its "
+           f"own stream from {run['side_stream_min_t']} tokens), then {ks} per-call event steps with every call alone "
+           "on the launch stream. The last column averages each kernel's dispatches in those last "
+           f"{ks} forwards; it is what the bench line's per-call times (HIP events between the calls) measure, "
+           "launch gaps included.", "",
+           "| kernel | calls | per forward | avg µs | min µs | max µs | % of GPU time | avg µs, last "
+           f"{ks} forwards (one stream) |", "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        c = int(r["Calls"])
+        ss = single_stream(r["Name"])
+        pf = f"{c // n_fwd}" if c % n_fwd == 0 else "–"
+        out.append(f"| `{short(r['Name'])}` | {c} | {pf} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} | "
+                   f"{'–' if ss is None else f'{ss:.1f}'} |")
+    rf = line["roofline"]
+    out += ["", "bench.py line of the same run (HIP events on the launch stream):", "",
+            f"- value {line['value']:.0f} tokens/s, {line['ms_per_step']:.3f} ms per layer step",
+            f"- dominant call `{rf['kernel']}`: {rf['kernel_ms'] * 1e3:.1f} µs per launch, {rf['achieved']:.1f} "
+            f"{rf['unit']} algorithmic of {rf['peak']:.1f} ({100 * rf['frac']:.1f}% of peak, bound {rf['bound']})",
+            "- per-call ms: " + ", ".join(f"{k} {v:.3f}" for k, v in line["kernel_ms"].items()), ""]
+    path = os.path.join(ROOT, "profiles", f"moe_layer_{cfg_name}_kernel_stats.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    print(f"wrote {path}")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -177,6 +362,11 @@ def main():
         if not args.calibrate_copy:
             sys.exit("--traffic-from needs --calibrate-copy MIB, the copy size of the counted run")
         write_traffic(args, cfg0)
+        return
+    if args.stats_from:
+        if not args.bench_json:
+            sys.exit("--stats-from needs --bench-json, the --json-out file of the profiled run")
+        stats_summary(args)
         return
     import torch
     from int4_routed_expert_moe_amd.layer import MoELayer
@@ -206,48 +396,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        layer.forward(x)
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        layer.forward(x)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / args.steps
-
-    # per-call durations from events recorded between the calls, on the launch stream
-    per = {}
-    for _ in range(args.kernel_steps):
-        marks = []
-        layer.forward(x, marks=marks)
-        torch.cuda.synchronize()
-        for (_, a), (name, b) in zip(marks[:-1], marks[1:]):
-            per.setdefault(name, []).append(a.elapsed_time(b))
-    kernel_ms = {n: float(np.mean(v)) for n, v in per.items()}
-
-    ws = layer.workspace(T)
-    counts = ws["counts"].cpu().numpy()
-    work, layer_bytes, layer_flops, active = algorithmic_work(cfg, counts, cfg["shared_I"])
-    dom = max((n for n in kernel_ms if n in work), key=lambda n: kernel_ms[n])
-    b, f = work[dom]
-    dur_s = kernel_ms[dom] / 1e3
-    intensity = f / max(b, 1)
-    if intensity < MFMA_F16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "hbm", "achieved": b / dur_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": f / dur_s / 1e12, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_record(dom, cfg["name"])
-    roof["kernel"] = dom
-    roof["kernel_ms"] = kernel_ms[dom]
-    roof["algorithmic_bytes"] = b
-    roof["algorithmic_flops"] = f
+    ms_per_step, kernel_ms, wall = time_layer(layer, x, args.steps, args.warmup, args.kernel_steps)
+    counts = layer.workspace(T)["counts"].cpu().numpy()
+    roof, layer_bytes, layer_flops, active = roofline(cfg, counts, kernel_ms)
 
     step_s = ms_per_step / 1e3
     line = {
@@ -281,9 +432,36 @@ def main():
         "kernel_ms": kernel_ms,
         "wall_s_timed": wall,
         "setup_s": t_gen,
+        "run": {"warmup": args.warmup, "steps": args.steps, "kernel_steps": args.kernel_steps,
+                "side_stream_min_t": MoELayer.SIDE_STREAM_MIN_T},
     }
     if cfg["mode"] == "exact":
         line["layer_roofline"]["int8_frac"] = layer_flops / step_s / (INT8_PEAK_TOPS * 1e12)
+
+    prefill_leg = args.prefill_leg if args.prefill_leg is not None else (args.workload == 2 and args.act_bits is None)
+    if prefill_leg:
+        # the same layer (workloads 2 and 3 share their weights) at prefill size
+        cfg3 = dict(synthetic.WORKLOADS[3])
+        if cfg3["layer_seed"] != cfg["layer_seed"] or cfg3["H"] != cfg["H"]:
+            sys.exit("--prefill-leg needs a workload that shares the prefill workload's layer")
+        x3 = torch.from_numpy(synthetic.gen_x(cfg3).view(np.int16)).cuda().view(torch.bfloat16)
+        ms3, kms3, wall3 = time_layer(layer, x3, args.steps, args.warmup, max(3, args.kernel_steps // 2))
+        counts3 = layer.workspace(cfg3["T"])["counts"].cpu().numpy()
+        roof3, lb3, lf3, active3 = roofline(cfg3, counts3, kms3)
+        line["prefill"] = {
+            "workload": f"{cfg3['name']}: T={cfg3['T']} (the same layer, weights shared with the headline workload)",
+            "value": cfg3["T"] / (ms3 / 1e3), "unit": "tokens/s", "ms_per_step": ms3, "steps": args.steps,
+            "warmup": args.warmup, "wall_s_timed": wall3, "active_experts": active3, "roofline": roof3,
+            "layer_roofline": {"bytes": lb3, "flops": lf3, "mfma_frac": lf3 / (ms3 / 1e3) / (MFMA_F16_PEAK_TFS * 1e12),
+                               "hbm_frac": lb3 / (ms3 / 1e3) / (HBM_PEAK_GBS * 1e9)},
+            "kernel_ms": kms3,
+        }
+        del x3
+        layer._ws.pop(cfg3["T"], None)
+        torch.cuda.empty_cache()
+
+    if not args.no_hbm_probe:
+        line["hbm_probe"] = hbm_probe()
 
     if not args.no_cpu_baseline:
         import oracle
@@ -298,10 +476,15 @@ def main():
         el = time.perf_counter() - t0
         line["cpu_baseline"] = {
             "value": len(toks) / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{len(toks)} of {T} tokens of the same workload (routing of the sampled tokens "
                       f"included), {el:.1f} s",
         }
-    print(json.dumps(line))
+    text = json.dumps(line)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(text + "\n")
+    print(text)
 
 
 if __name__ == "__main__":

@@ -34,9 +34,13 @@
  *    This is the checkpoint layout.  The grouped expert GEMMs read the same
  *    bytes in the fragment layout made once by moe_int4_prepack (below).
  *  - Numerics of the routed GEMMs: operands are fp16 on the matrix cores.
- *    Activations must lie within the fp16 finite range (|v| < 65504; larger
- *    values saturate) and bf16 scales within [2^-14, 2^9] (outside it the
- *    dequantised operand loses exactness).
+ *    bf16 activations are converted rounding toward zero: magnitudes in
+ *    [2^-14, 65504] convert exactly, smaller ones become fp16 subnormals
+ *    (absolute error below 2^-24) and larger ones saturate to 65504; with
+ *    the fp16 staging format (MOE_MODE_BF16_F16P) the same holds for h.
+ *    bf16 scales must be 0 or of magnitude in [2^-14, 2^9], where q * s is
+ *    exact in fp16; moe_int4_check_scales checks a scale tensor once at
+ *    weight load.
  *  - Shape limits (else MOE_ERR_UNSUPPORTED): 1 <= k <= min(E, 16), E <= 1024,
  *    T*k < 2^31; H and I multiples of 128; expert-output widths (I for
  *    gate/up, H for down) multiples of 128 and 256 respectively; dense
@@ -183,6 +187,17 @@ int moe_quant_act_int16(const uint16_t* x, int M, int K, int16_t* q, float* s, v
  * must not overlap.  E == 0 is a no-op. */
 int moe_int4_prepack(const uint8_t* packed, const uint16_t* scale, int E, int N, int K,
                      uint8_t* packed_out, uint16_t* scale_out, void* stream);
+
+/* Load-time check of a scale tensor for the routed GEMMs (the checkpoint's
+ * weight_scale of "Kimi exact-generator adaptation", "Sources & provenance",
+ * loaded without conversion): counts the bf16 scales that are neither zero
+ * nor of magnitude in [2^-14, 2^9] (NaN and infinity included) into *count
+ * (device int32, 4-byte aligned, overwritten) and returns MOE_ERR_UNSUPPORTED
+ * with the count in the error detail when there is any, else MOE_OK.  scale
+ * is n bf16 values (2-byte aligned), in either layout.  Unlike every other
+ * call it synchronises `stream` to return its verdict: a weight-load step,
+ * not for the forward path.  n == 0 returns MOE_OK. */
+int moe_int4_check_scales(const uint16_t* scale, size_t n, int32_t* count, void* stream);
 
 /* ---------------------------------------------------------------------------
  * fp16 staging format of activations (an implementation layout, not from the

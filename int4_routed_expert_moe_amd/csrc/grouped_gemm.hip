@@ -40,6 +40,7 @@
 // fma(s_w*G, s_x, acc), groups ascending.  With 16-bit activation codes the
 // high and low bytes are two exact fp16 operand planes and two steps per group
 // give s_w*G_hi and s_w*G_lo, joined exactly as fma(s_w*G_hi, 256, s_w*G_lo).
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -1348,6 +1349,30 @@ __global__ __launch_bounds__(256) void k_prepack_s(const uint16_t* __restrict__ 
     *reinterpret_cast<u32x2_t*>(dst + (size_t)t * 4) = v;
 }
 
+// Scale range check: a bf16 scale keeps the fp16 dequantisation exact when it
+// is zero or its magnitude lies in [2^-14, 2^9] (bf16 bits 0x3880..0x4400).
+__device__ __forceinline__ bool scale_in_range(uint32_t bits) {
+    const uint32_t a = bits & 0x7FFFu;
+    return a == 0 || (a >= 0x3880u && a <= 0x4400u);
+}
+
+__global__ __launch_bounds__(64) void k_zero_count(int32_t* __restrict__ count) {
+    if (threadIdx.x == 0) count[0] = 0;
+}
+
+// Counts the out-of-range scales: one ballot per wave and step, one atomic add
+// per wave at the end.
+__global__ __launch_bounds__(256) void k_count_bad_scales(const uint16_t* __restrict__ scale, long n,
+                                                         int32_t* __restrict__ count) {
+    const long stride = (long)gridDim.x * 256;
+    int bad = 0;
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i - threadIdx.x % MOE_WAVE < n; i += stride) {
+        const bool b = i < n && !scale_in_range(scale[i]);
+        bad += __popcll(__ballot(b));
+    }
+    if (lane_id() == 0 && bad) atomicAdd(count, bad);
+}
+
 // Activations into the fp16 staging format: one 8-element block per thread.
 __global__ __launch_bounds__(256) void k_act_f16p(const u32x4_t* __restrict__ x, u32x4_t* __restrict__ out, long blocks) {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -1440,6 +1465,10 @@ int launch_grouped(GroupedArgs& a, int S, hipStream_t st, const char* what) {
     return moe::launch_status(what);
 }
 
+// The kernels address one expert's packed matrix (N x K/2 bytes) with 32-bit
+// byte counts and int offsets: it must stay below 2 GiB.
+bool expert_fits_offsets(int N, int K) { return (size_t)N * (size_t)(K / 2) < ((size_t)1 << 31); }
+
 int check_common(const char* what, int mode, int T, int k, int E) {
     using namespace moe;
     if (mode != MOE_MODE_BF16 && mode != MOE_MODE_EXACT_I8 && mode != MOE_MODE_BF16_F16P &&
@@ -1464,6 +1493,8 @@ extern "C" int moe_int4_grouped_swiglu(int mode, const void* act, const float* a
     if (int rc = check_common(what, mode, T, k, E)) return rc;
     if (H <= 0 || I <= 0 || H % kKC != 0 || I % 128 != 0)
         return fail(MOE_ERR_UNSUPPORTED, "%s: H=%d (multiple of 128) I=%d (multiple of 128)", what, H, I);
+    if (!expert_fits_offsets(I, H))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: one expert's %d x %d matrix is 2 GiB or more", what, I, H);
     if (T == 0) return MOE_OK;
     if (!act || !gate_packed || !gate_scale || !up_packed || !up_scale || !offsets || !sorted_slot || !h)
         return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
@@ -1506,6 +1537,8 @@ extern "C" int moe_int4_grouped_down(int mode, const void* h, const float* h_sca
     if (int rc = check_common(what, mode, T, k, E)) return rc;
     if (H <= 0 || I <= 0 || I % kKC != 0 || H % 256 != 0)
         return fail(MOE_ERR_UNSUPPORTED, "%s: I=%d (multiple of 128) H=%d (multiple of 256)", what, I, H);
+    if (!expert_fits_offsets(H, I))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: one expert's %d x %d matrix is 2 GiB or more", what, H, I);
     if (T == 0) return MOE_OK;
     if (!h || !down_packed || !down_scale || !offsets || !y)
         return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
@@ -1548,6 +1581,29 @@ extern "C" int moe_act_f16p(const uint16_t* x, int rows, int K, uint16_t* out, v
     hipLaunchKernelGGL(k_act_f16p, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, as_stream(stream),
                        reinterpret_cast<const u32x4_t*>(x), reinterpret_cast<u32x4_t*>(out), blocks);
     return launch_status(what);
+}
+
+extern "C" int moe_int4_check_scales(const uint16_t* scale, size_t n, int32_t* count, void* stream) {
+    using namespace moe;
+    const char* what = "moe_int4_check_scales";
+    if (n == 0) return MOE_OK;
+    if (!scale || !count) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+    if ((reinterpret_cast<uintptr_t>(scale) & 1) || (reinterpret_cast<uintptr_t>(count) & 3))
+        return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer", what);
+    hipStream_t st = as_stream(stream);
+    hipLaunchKernelGGL(k_zero_count, dim3(1), dim3(64), 0, st, count);
+    if (int rc = launch_status(what)) return rc;
+    const long blocks = std::min<long>(2048, ((long)n + 255) / 256);
+    hipLaunchKernelGGL(k_count_bad_scales, dim3((unsigned)blocks), dim3(256), 0, st, scale, (long)n, count);
+    if (int rc = launch_status(what)) return rc;
+    int32_t host = 0;
+    hipError_t e = hipMemcpyAsync(&host, count, sizeof host, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    if (host != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: %d of %zu scales are neither 0 nor of magnitude in [2^-14, 2^9]", what,
+                    host, n);
+    return MOE_OK;
 }
 
 extern "C" int moe_int4_prepack(const uint8_t* packed, const uint16_t* scale, int E, int N, int K,

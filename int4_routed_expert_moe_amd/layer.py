@@ -43,8 +43,9 @@ def prepack_experts(ex: dict) -> dict:
 class MoELayer:
     """Routed int4 experts + shared bf16 expert (+ optional K3 latent wrapper).
 
-    `experts` holds the routed weights in the checkpoint layout; they are
-    permuted once into the fragment layout here."""
+    `experts` holds the routed weights in the checkpoint layout; their scales
+    are checked (moe_int4_check_scales) and they are permuted once into the
+    fragment layout here."""
 
     SIDE_STREAM_MIN_T = 64  # tokens from which the shared expert runs on its own stream
     # tokens from which the bf16 expert input is converted once to the fp16 staging
@@ -61,6 +62,10 @@ class MoELayer:
             self.mode = _m.MOE_MODE_BF16
         self.router_w = router_w
         self.router_b = router_b
+        # weight load: the scales must keep the fp16 dequantisation exact
+        count = torch.empty(1, dtype=torch.int32, device=router_w.device)
+        for name in ("sg", "su", "sd"):
+            _m.moe_int4_check_scales(experts[name], count)
         self.ex = prepack_experts(experts)
         self.shared = shared
         self.latent = latent

@@ -48,6 +48,7 @@ EXPORTS = {
     "moe_permute_noalloc": ([_P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "moe_quant_act_int8": ([_P, _I, _I, _P, _P, _P], _I),
     "moe_int4_prepack": ([_P, _P, _I, _I, _I, _P, _P, _P], _I),
+    "moe_int4_check_scales": ([_P, _SZ, _P, _P], _I),
     "moe_act_f16p": ([_P, _I, _I, _P, _P], _I),
     "moe_quant_act_int16": ([_P, _I, _I, _P, _P, _P], _I),
     "moe_exact_linear_i8w": ([_P, _P, _P, _P, _I, _I, _I, _P, _P], _I),
@@ -205,6 +206,16 @@ def moe_int4_prepack(packed, scale, packed_out, scale_out):
     _need(scale_out, torch.bfloat16, (E, N, K // 32), "scale_out")
     _check("moe_int4_prepack", _lib.moe_int4_prepack(_ptr(packed), _ptr(scale), E, N, K, _ptr(packed_out),
                                                      _ptr(scale_out), _stream()))
+
+
+def moe_int4_check_scales(scale, count=None):
+    """Raise MoEError (MOE_ERR_UNSUPPORTED) when a bf16 scale tensor holds values that
+    are neither 0 nor of magnitude in [2^-14, 2^9]; synchronises the current stream."""
+    _need(scale, torch.bfloat16, None, "scale")
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=scale.device)
+    _need(count, torch.int32, (1,), "count")
+    _check("moe_int4_check_scales", _lib.moe_int4_check_scales(_ptr(scale), scale.numel(), _ptr(count), _stream()))
 
 
 _ACT_DTYPE = {MOE_MODE_BF16: torch.bfloat16, MOE_MODE_EXACT_I8: torch.int8, MOE_MODE_BF16_F16P: torch.float16,

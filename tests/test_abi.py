@@ -99,8 +99,20 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert _status(lib, g, 0, fake, fake, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
     assert _status(lib, g, 1, fake, null, fake, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
     assert _status(lib, g, 0, fake, null, null, fake, fake, fake, fake, fake, 4, 2, 16, 256, 128, fake, null, null) == -1
+    # one expert's packed matrix must stay below 2 GiB (32-bit addressing inside the kernels)
+    assert _status(lib, g, 0, fake, null, fake, fake, fake, fake, fake, fake, 4, 2, 16, 65536, 65536, fake, null, null) == -2
+    assert b"2 GiB" in lib.moe_last_error_detail()
     d = "moe_int4_grouped_down"
+    assert _status(lib, d, 0, fake, null, fake, fake, fake, 4, 2, 16, 65536, 65536, fake, null) == -2
+    assert b"2 GiB" in lib.moe_last_error_detail()
     assert _status(lib, d, 0, fake, null, fake, fake, fake, 4, 2, 16, 128, 384, fake, null) == -2
+    # scale check: null or misaligned pointers, and nothing to check
+    cs = "moe_int4_check_scales"
+    lib.moe_int4_check_scales.argtypes = [P, ctypes.c_size_t, P, P]
+    assert _status(lib, cs, null, 16, fake, null) == -1
+    assert _status(lib, cs, P(0x1001), 16, fake, null) == -1
+    assert _status(lib, cs, fake, 16, P(0x1002), null) == -1
+    assert _status(lib, cs, null, 0, null, null) == 0
     assert _status(lib, d, 1, fake, null, fake, fake, fake, 4, 2, 16, 128, 256, fake, null) == -1
     # combine: exact mode with a shared input, misaligned output
     assert _status(lib, "moe_combine", 1, fake, fake, fake, fake, 4, 2, 256, fake, null) == -1

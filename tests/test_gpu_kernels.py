@@ -594,3 +594,23 @@ def test_rmsnorm(m, M, N, seed):
     diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
     assert diff.max() <= 1, "rmsnorm differs by more than one bf16 step"
     np.testing.assert_array_equal(got[0], ref[0])
+
+
+def test_check_scales(m):
+    """The load-time scale check: zeros and magnitudes in [2^-14, 2^9] pass; the first
+    values outside (either side), NaN and infinity are counted."""
+    say("check scales")
+    good = np.array([0.0, -0.0, 2.0 ** -14, -(2.0 ** -14), 2.0 ** 9, -(2.0 ** 9), 0.01, 300.0], np.float32)
+    bad = np.array([2.0 ** 9 * (1 + 2.0 ** -7), 2.0 ** -15, -(2.0 ** 10), np.inf, -np.inf, np.nan], np.float32)
+    g = np.random.default_rng(0)
+    base = refmath.bf16_from_f32(g.uniform(0.005, 0.02, 100000).astype(np.float32))
+    ok = np.concatenate([base, refmath.bf16_from_f32(good)])
+    m.moe_int4_check_scales(bf16_dev(ok))
+    for i in range(len(bad)):
+        arr = ok.copy()
+        pos = g.integers(0, len(arr), 1 + i)
+        arr[pos] = refmath.bf16_from_f32(np.full(len(pos), bad[i], np.float32))
+        with pytest.raises(m.MoEError) as ei:
+            m.moe_int4_check_scales(bf16_dev(arr))
+        assert ei.value.status == m.MOE_ERR_UNSUPPORTED
+        assert f" {len(np.unique(pos))} of {len(arr)} " in str(ei.value)

@@ -216,3 +216,66 @@ def test_layer_switches(renormalize, latent_norm, latent):
     other = oracle.layer_tokens(dict(inp, cfg=dict(cfg, renormalize=True, latent_norm=True)), np.arange(4))
     if not (renormalize and latent_norm):
         assert (other != ref[:4]).any()
+
+
+def test_layer_rejects_out_of_range_scales():
+    from int4_routed_expert_moe_amd import moe as _m
+    from int4_routed_expert_moe_amd.layer import MoELayer
+    base = inputs(1)
+    ex = dict(base["experts"])
+    sd = ex["sd"].copy()
+    sd[3, 5, 1] = 0x4480  # bf16 1024.0, past 2^9
+    ex["sd"] = sd
+    say("layer load with an out-of-range down scale")
+    with pytest.raises(_m.MoEError) as ei:
+        MoELayer.from_numpy(dict(base, experts=ex), "cuda")
+    assert ei.value.status == _m.MOE_ERR_UNSUPPORTED
+
+
+def test_layer_activation_beyond_fp16_range():
+    """An activation past the fp16 range saturates to 65504 in the routed experts (the
+    documented conversion), while the router sees it as it is.  The tiny layer without
+    its shared expert, token 9 with x[37] = 2^17 and x[38] = 0, and weight column 38 a
+    copy of column 37 in every gate/up row: the GPU output of that token matches the
+    oracle given x[37] = 65280 and x[38] = 224 (bf16 values whose products with the
+    shared column sum to 65504 times it), with the routing of the real input, and is far
+    from the oracle given the real value.  Every other token matches as usual.  Column
+    37's scale group gets the smallest exact scale (2^-14) in every gate/up row, so h
+    stays inside the fp16 range of the down projection's operands."""
+    from int4_routed_expert_moe_amd.layer import MoELayer
+    base = inputs(1)
+    t, i = 9, 37
+    ex = dict(base["experts"])
+    for n in ("sg", "su"):
+        sc = ex[n].copy()
+        sc[:, :, i // 32] = 0x3880
+        ex[n] = sc
+    for n in ("wg", "wu"):
+        w = ex[n].copy()
+        hi37 = w[:, :, i // 2] >> 4                  # element 37: high nibble of byte 18
+        w[:, :, (i + 1) // 2] = (w[:, :, (i + 1) // 2] & 0xF0) | hi37  # element 38: low nibble of byte 19
+        ex[n] = w
+    x = base["x"].copy()
+    x[t, i] = 0x4800      # bf16 2^17
+    x[t, i + 1] = 0       # 0.0
+    inp = dict(base, shared=None, experts=ex, x=x, cfg=dict(base["cfg"], shared_I=None))
+    L = MoELayer.from_numpy(inp, "cuda")
+    say("tiny layer (no shared expert) with one activation of 2^17")
+    out = L.forward(bf16_dev(x))
+    torch.cuda.synchronize()
+    T, k = inp["cfg"]["T"], inp["cfg"]["k"]
+    ridx, rw = oracle.route(x, inp["router_w"], inp["router_b"], k, True)
+    ws = L.workspace(T)
+    np.testing.assert_array_equal(ws["topk_idx"].cpu().numpy(), ridx)
+    got = np_bf16(out)
+    others = np.array([s for s in range(T) if s != t])
+    ref = oracle.layer_tokens(inp, others, topk_idx=ridx, topk_w=rw)
+    assert_bf16_close(got[others], ref, "other tokens")
+    x_sat = x.copy()
+    x_sat[t, i] = 0x477F      # bf16 65280
+    x_sat[t, i + 1] = 0x4360  # bf16 224
+    ref_sat = oracle.layer_tokens(dict(inp, x=x_sat), [t], topk_idx=ridx, topk_w=rw)
+    assert_bf16_close(got[t:t + 1], ref_sat, "saturated token")
+    ref_raw = oracle.layer_tokens(inp, [t], topk_idx=ridx, topk_w=rw)
+    with pytest.raises(AssertionError):
+        assert_bf16_close(got[t:t + 1], ref_raw, "unsaturated reference")
