@@ -196,6 +196,17 @@ __device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2, half2_t c2) 
     return r;
 }
 
+// Pair Q (0..3) of dequant8: elements (Q, Q+4) of dword w, the same three
+// operations, so that a caller can spread one dword's conversion over several
+// matrix-core operations.
+template <int Q>
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, half2_t s2, half2_t c2) {
+    const uint32_t M = 0x03C003C0u;
+    const uint32_t X = 0x4E004E00u;
+    const uint32_t sh = Q == 0 ? (w << 6) : Q == 1 ? (w << 2) : Q == 2 ? (w >> 2) : (w >> 6);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, (sh & M) ^ X), s2, c2));
+}
+
 // bf16 scale bits -> (s, s) and (-24 s, -24 s) in fp16.
 __device__ __forceinline__ void scale_pair(uint32_t sbits, half2_t& s2, half2_t& c2) {
     const float s = bf16_bits_to_f32(sbits & 0xFFFFu);
@@ -241,6 +252,20 @@ __device__ __forceinline__ void store_h(void* out, size_t row_base, int col, uin
         static_cast<uint16_t*>(out)[row_base + f16p_col(col)] = bf16_to_f16_bits(hb);
     else
         static_cast<uint16_t*>(out)[row_base + col] = (uint16_t)hb;
+}
+
+// bf16 path helpers (its outputs are compared within a tolerance; the exact
+// path keeps the pinned moe_silu).  SiLU on the hardware exp2 and reciprocal,
+// a few fp32 ulps, far below a bf16 step; and the gfx950 packed conversion of
+// two fp32 values to bf16, round to nearest even like f32_to_bf16_bits.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float silu_fast(float z) {
+    const float e = __builtin_amdgcn_exp2f(-z * 1.44269504088896341f);
+    return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // 8 int8 (2 dwords, elements in order) -> 8 exact fp16 integers in pair order.
@@ -411,7 +436,12 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
             sl.S[cb] = __builtin_amdgcn_raw_buffer_load_b64(second ? rs1 : rs0, lane_s, soff[cb] + c * (kFragScales * 2), 0);
         }
     };
-    u32x4_t Aq[A_ITERS];
+    // activation chunks in flight in registers: bf16 loads chunk c+2 while chunk c
+    // is multiplied (the gathered rows come from L2 or HBM, whose latency one
+    // chunk of products does not cover); exact mode, whose chunks are long
+    // (VALU folds) and registers tight, chunk c+1
+    constexpr int ADEPTH = EXACT ? 1 : 2;
+    u32x4_t Aq[ADEPTH][A_ITERS];
     f32x4_t SXq = {0.f, 0.f, 0.f, 0.f};
     // With NACT > 0 active row blocks known at compile time, staging instructions
     // whose rows all lie past them are skipped (wave-uniform branches): their
@@ -420,36 +450,39 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
         constexpr int NACT = decltype(nact)::value;
         return NACT == 0 || A_ITERS * RPI * wave + RPI * it < 16 * NACT;
     };
-    auto load_A = [&](int c, auto nact) __attribute__((always_inline)) {
+    auto load_A = [&](int c, auto nact, auto slotc) __attribute__((always_inline)) {
         constexpr int NACT = decltype(nact)::value;
+        constexpr int SL = decltype(slotc)::value;
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
             if (!staged(nact, it)) continue;
             if (!EXACT || ACT16)
-                Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + aoff[it] + c * kKC);
+                Aq[SL][it] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.act) + aoff[it] + c * kKC);
             else
-                Aq[it] = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + aoff[it] + c * kKC);
+                Aq[SL][it] = *reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(a.act) + aoff[it] + c * kKC);
         }
         if (EXACT && tid < (NACT > 0 ? 16 * NACT : BM))
             SXq = *reinterpret_cast<const f32x4_t*>(a.act_scale + (size_t)sxrow * (K / 32) + c * 4);
     };
-    auto store_A = [&](int buf, auto nact) __attribute__((always_inline)) {
+    auto store_A = [&](int buf, auto nact, auto slotc) __attribute__((always_inline)) {
         constexpr int NACT = decltype(nact)::value;
+        constexpr int SL = decltype(slotc)::value;
 #pragma unroll
         for (int it = 0; it < A_ITERS; ++it) {
             if (!staged(nact, it)) continue;
             const int row = srow_of(it);
             const int piece = lane % PIECES;
+            const u32x4_t q = Aq[SL][it];
             if (ACT16) {
                 u32x4_t hi, lo;
-                i16x8_to_f16_hilo(Aq[it], hi, lo);
+                i16x8_to_f16_hilo(q, hi, lo);
                 *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = hi;
                 *reinterpret_cast<u32x4_t*>(&As2[ACT16 ? buf : 0][ACT16 ? row : 0][piece * 8]) = lo;
             } else if (!EXACT) {
-                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = F16P ? Aq[it] : bf16x8_to_f16_perm(Aq[it]);
+                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 8]) = F16P ? q : bf16x8_to_f16_perm(q);
             } else {
-                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16]) = i8x8_to_f16_perm(Aq[it][0], Aq[it][1]);
-                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16 + 8]) = i8x8_to_f16_perm(Aq[it][2], Aq[it][3]);
+                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16]) = i8x8_to_f16_perm(q[0], q[1]);
+                *reinterpret_cast<u32x4_t*>(&As[buf][row][piece * 16 + 8]) = i8x8_to_f16_perm(q[2], q[3]);
             }
         }
         if (EXACT && tid < (NACT > 0 ? 16 * NACT : BM)) {
@@ -587,28 +620,34 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
     // chunks are long (VALU folds), two, which keeps its registers within two
     // waves per SIMD.
     constexpr int RING = EXACT ? 2 : 3;
+    constexpr int UNROLL = RING * ADEPTH / (RING % ADEPTH == 0 ? ADEPTH : 1);  // lcm(RING, ADEPTH), ADEPTH <= 2
     auto main_loop = [&](auto nact) __attribute__((always_inline)) {
         Slot sl[RING];
-        load_A(0, nact);
+        load_A(0, nact, std::integral_constant<int, 0>{});
 #pragma unroll
         for (int i = 0; i < RING; ++i) load_B(min(i, nch - 1), sl[i]);
-        store_A(0, nact);
+        if constexpr (ADEPTH == 2) load_A(min(1, nch - 1), nact, std::integral_constant<int, 1>{});
+        store_A(0, nact, std::integral_constant<int, 0>{});
         lds_barrier();
-        auto step = [&](int c, Slot& cur) __attribute__((always_inline)) {
-            load_A(min(c + 1, nch - 1), nact);
+        // step c: load chunk c+ADEPTH into the register slot chunk c left (it is in
+        // LDS already), multiply chunk c, refill the weight slot, write chunk c+1
+        // (loaded ADEPTH-1 steps ago) to the other LDS buffer
+        auto step = [&](int c, auto ic) __attribute__((always_inline)) {
+            constexpr int I = decltype(ic)::value;
+            load_A(min(c + ADEPTH, nch - 1), nact, std::integral_constant<int, I % ADEPTH>{});
             __builtin_amdgcn_sched_barrier(0);
-            compute(nact, c, cur);
+            compute(nact, c, sl[I % RING]);
             __builtin_amdgcn_sched_barrier(0);
-            load_B(min(c + RING, nch - 1), cur);
+            load_B(min(c + RING, nch - 1), sl[I % RING]);
             __builtin_amdgcn_sched_barrier(0);
-            store_A((c + 1) & 1, nact);
+            store_A((c + 1) & 1, nact, std::integral_constant<int, (I + 1) % ADEPTH>{});
             lds_barrier();
         };
         int c = 0;
-        for (; c + RING <= nch; c += RING)
-            static_for<RING>([&](auto ic) __attribute__((always_inline)) { step(c + decltype(ic)::value, sl[decltype(ic)::value]); });
-        static_for<RING - 1>([&](auto ic) __attribute__((always_inline)) {
-            if (c + decltype(ic)::value < nch) step(c + decltype(ic)::value, sl[decltype(ic)::value]);
+        for (; c + UNROLL <= nch; c += UNROLL)
+            static_for<UNROLL>([&](auto ic) __attribute__((always_inline)) { step(c + decltype(ic)::value, ic); });
+        static_for<UNROLL - 1>([&](auto ic) __attribute__((always_inline)) {
+            if (c + decltype(ic)::value < nch) step(c + decltype(ic)::value, ic);
         });
     };
     if constexpr (EXACT) {
@@ -634,10 +673,12 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
                 if (!EXACT) {
 #pragma unroll
                     for (int p = 0; p < CB / 2; ++p) {
-                        const uint32_t gb = f32_to_bf16_bits(acc[mb][p][i]);
-                        const uint32_t ub = f32_to_bf16_bits(acc[mb][CB / 2 + p][i]);
-                        const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
-                        const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
+                        // g and u rounded to bf16 by one packed conversion, SiLU on the
+                        // hardware exp2 and reciprocal (bf16 path)
+                        const uint32_t v = bf16x2_bits(acc[mb][p][i], acc[mb][CB / 2 + p][i]);
+                        const float g = __uint_as_float(v << 16), u = __uint_as_float(v & 0xFFFF0000u);
+                        const uint32_t ab = bf16x2_bits(silu_fast(g), 0.0f) & 0xFFFFu;
+                        const uint32_t hb = bf16x2_bits(__uint_as_float(ab << 16) * u, 0.0f) & 0xFFFFu;
                         if (ok) store_h<F16P>(a.out, orow * N, n0 + 16 * p + r, hb);
                     }
                 } else {
@@ -695,6 +736,39 @@ __global__ __launch_bounds__(256) void k_grouped(GroupedArgs a) {
 template <int MODE, int OP, int MB, int CB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_grouped_exact(GroupedArgs a) {
     grouped_tile<MODE, OP, MB, CB>(a);
+}
+
+// Epilogue of the 32x32 tile kernels: element i of lane l is tile row
+// 32 mb + 8(i/4) + 4 kb + i%4, column c32 of each column block.  Gate/up:
+// h = bf16(bf16(silu(g)) * u) from g = bf16(gate sum), u = bf16(up sum)
+// (both converted by one packed instruction), stored as bf16 or in the fp16
+// staging format; down: the two column blocks' sums as bf16.
+template <bool GATEUP, bool F16P, int M32>
+__device__ __forceinline__ void epilogue32(const GroupedArgs& a, const TileInfo& ti, int n0, int c32, int kb,
+                                           const f32x16_t (&acc)[M32][2]) {
+    const int N = a.N;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + (size_t)ti.row0 * (size_t)N +
+                    (GATEUP && F16P ? f16p_col(n0 + c32) : n0 + c32);
+#pragma unroll
+    for (int mb = 0; mb < M32; ++mb) {
+        if (32 * mb >= ti.rows) break;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
+            if (rl >= ti.rows) continue;
+            uint16_t* o = out + (size_t)rl * (size_t)N;
+            const uint32_t v = bf16x2_bits(acc[mb][0][i], acc[mb][1][i]);
+            if constexpr (GATEUP) {
+                const float g = __uint_as_float(v << 16), u = __uint_as_float(v & 0xFFFF0000u);
+                const uint32_t ab = bf16x2_bits(silu_fast(g), 0.0f) & 0xFFFFu;
+                const uint32_t hb = bf16x2_bits(__uint_as_float(ab << 16) * u, 0.0f) & 0xFFFFu;
+                o[0] = F16P ? bf16_to_f16_bits(hb) : (uint16_t)hb;
+            } else {
+                o[0] = (uint16_t)(v & 0xFFFFu);
+                o[32] = (uint16_t)(v >> 16);
+            }
+        }
+    }
 }
 
 // Large bf16 tiles on the 32x32x16 matrix-core shape (one wave per SIMD drives
@@ -804,14 +878,16 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
             for (int i = 0; i < 16; ++i) acc[mb][cb][i] = 0.0f;
 
     // dequantised operands of K step s (column blocks 0, 1)
-    auto dequant_k = [&](const Slot& sl, int st, half8_t (&bf)[2]) __attribute__((always_inline)) {
+    // Piece J (0..7) of K step st's dequantised operands: column block J/4, pair
+    // J%4 (three VALU operations); the group's scale pair is converted at the
+    // block's first piece of the group's first step and kept for its second.
+    auto dq_piece = [&](const Slot& sl, int st, auto jc, half2_t (&s2)[2], half2_t (&c2)[2],
+                        u32x4_t (&bf)[2]) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int cb = J >> 2, q = J & 3;
         const int g = st >> 1;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            half2_t s2, c2;
-            scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
-            bf[cb] = dequant8(sl.B[cb][st & 1][g], s2, c2);
-        }
+        if (q == 0 && (st & 1) == 0) scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2[cb], c2[cb]);
+        bf[cb][q] = dequant_pair<q>(sl.B[cb][st & 1][g], s2[cb], c2[cb]);
     };
     // One stream of 8*NACT (K step, row block) products over the tile's NACT
     // active row blocks (blocks wholly past its rows are skipped); fragment
@@ -837,8 +913,12 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
         half8_t afr[NS];
 #pragma unroll
         for (int q = 0; q < PF; ++q) afr[q] = frag(q);
-        half8_t bfa[2], bfb[2];
-        dequant_k(sl, 0, bfa);
+        // the next step's operands are converted in 8 pieces spread evenly over
+        // this step's products (piece J at product J*NACT/8): a clump of all 8 at
+        // one product outlasts the matrix-core operations around it
+        u32x4_t bfa[2], bfb[2];
+        half2_t s2[2], c2[2];
+        static_for<8>([&](auto jc) __attribute__((always_inline)) { dq_piece(sl, 0, jc, s2, c2, bfa); });
         static_for<NS>([&](auto pc) __attribute__((always_inline)) {
             constexpr int p = decltype(pc)::value;
             constexpr int st = p / NACT;
@@ -851,12 +931,18 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
                     load_piece(i, min(c + 2, nch - 1));
                 }
             });
-            if constexpr (mb == 0 && st < 7) dequant_k(sl, st + 1, (st & 1) ? bfa : bfb);
-            half8_t(&cur)[2] = (st & 1) ? bfb : bfa;
+            if constexpr (st < 7) {
+                static_for<8>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int J = decltype(jc)::value;
+                    if constexpr (J * NACT / 8 == mb) dq_piece(sl, st + 1, jc, s2, c2, (st & 1) ? bfa : bfb);
+                });
+            }
+            u32x4_t(&cur)[2] = (st & 1) ? bfb : bfa;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
-                acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[p], cur[cb], acc[mb][cb], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0x0002);
+                acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[p], __builtin_bit_cast(half8_t, cur[cb]),
+                                                                      acc[mb][cb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         });
     };
 
@@ -894,28 +980,7 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
         if (nact == n) main_loop(std::integral_constant<int, n>{});
     });
 
-    // epilogue: element i of lane l is tile row 32 mb + 8(i/4) + 4 kb + i%4, column c32
-#pragma unroll
-    for (int mb = 0; mb < M32; ++mb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
-            if (rl >= ti.rows) continue;
-            const size_t orow = (size_t)(ti.row0 + rl);
-            if (GATEUP) {
-                const uint32_t gb = f32_to_bf16_bits(acc[mb][0][i]);
-                const uint32_t ub = f32_to_bf16_bits(acc[mb][1][i]);
-                const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
-                const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
-                store_h<F16P>(a.out, orow * N, n0 + c32, hb);
-            } else {
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-                    static_cast<uint16_t*>(a.out)[orow * N + n0 + 32 * cb + c32] =
-                        (uint16_t)f32_to_bf16_bits(acc[mb][cb][i]);
-            }
-        }
-    }
+    epilogue32<GATEUP, F16P, M32>(a, ti, n0, c32, kb, acc);
 }
 
 // k_grouped32 for activations already in the fp16 staging format, with the
@@ -931,7 +996,7 @@ __global__ __launch_bounds__(256) void k_grouped32(GroupedArgs a) {
 // waits for its own loads of chunk c+1 (issued a whole chunk earlier) before
 // the barrier that ends step c.  Same products and results as k_grouped32.
 template <int OP, int M32>
-__global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
+__device__ __forceinline__ void grouped32_dma_tile(const GroupedArgs& a) {
     constexpr int BM = 32 * M32;
     constexpr bool GATEUP = OP == 0;
     constexpr int A_ITERS = BM / 16;  // staging instructions per wave per chunk (4 rows each)
@@ -1023,14 +1088,16 @@ __global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mb][cb][i] = 0.0f;
 
-    auto dequant_k = [&](const Slot& sl, int st, half8_t (&bf)[2]) __attribute__((always_inline)) {
+    // Piece J (0..7) of K step st's dequantised operands: column block J/4, pair
+    // J%4 (three VALU operations); the group's scale pair is converted at the
+    // block's first piece of the group's first step and kept for its second.
+    auto dq_piece = [&](const Slot& sl, int st, auto jc, half2_t (&s2)[2], half2_t (&c2)[2],
+                        u32x4_t (&bf)[2]) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int cb = J >> 2, q = J & 3;
         const int g = st >> 1;
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            half2_t s2, c2;
-            scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2, c2);
-            bf[cb] = dequant8(sl.B[cb][st & 1][g], s2, c2);
-        }
+        if (q == 0 && (st & 1) == 0) scale_pair(sl.S[cb][g >> 1] >> (16 * (g & 1)), s2[cb], c2[cb]);
+        bf[cb][q] = dequant_pair<q>(sl.B[cb][st & 1][g], s2[cb], c2[cb]);
     };
     // One stream of 8*NACT (K step, row block) products reading tile buffer BUF;
     // the staging loads of chunk c+2 into buffer (BUF+2) mod 3 are spread over
@@ -1049,8 +1116,11 @@ __global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
         half8_t afr[NS];
 #pragma unroll
         for (int q = 0; q < PF; ++q) afr[q] = frag(q);
-        half8_t bfa[2], bfb[2];
-        dequant_k(sl, 0, bfa);
+        // the next step's operands in 8 pieces spread over this step's products,
+        // as in k_grouped32
+        u32x4_t bfa[2], bfb[2];
+        half2_t s2[2], c2[2];
+        static_for<8>([&](auto jc) __attribute__((always_inline)) { dq_piece(sl, 0, jc, s2, c2, bfa); });
         const int cs = min(c + 2, nch - 1);
         static_for<NS>([&](auto pc) __attribute__((always_inline)) {
             constexpr int p = decltype(pc)::value;
@@ -1062,12 +1132,18 @@ __global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
                 if constexpr (i * NS / (2 * A_ITERS) == p)
                     dma_piece(i, cs, std::integral_constant<int, (BUF + 2) % 3>{});
             });
-            if constexpr (mb == 0 && st < 7) dequant_k(sl, st + 1, (st & 1) ? bfa : bfb);
-            half8_t(&cur)[2] = (st & 1) ? bfb : bfa;
+            if constexpr (st < 7) {
+                static_for<8>([&](auto jc) __attribute__((always_inline)) {
+                    constexpr int J = decltype(jc)::value;
+                    if constexpr (J * NACT / 8 == mb) dq_piece(sl, st + 1, jc, s2, c2, (st & 1) ? bfa : bfb);
+                });
+            }
+            u32x4_t(&cur)[2] = (st & 1) ? bfb : bfa;
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb)
-                acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[p], cur[cb], acc[mb][cb], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0x0002);
+                acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[p], __builtin_bit_cast(half8_t, cur[cb]),
+                                                                      acc[mb][cb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         });
     };
 
@@ -1105,28 +1181,12 @@ __global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
         if (nact == n) main_loop(std::integral_constant<int, n>{});
     });
     wait_vmcnt<0>();  // the trailing (redundant) staging loads land before the wave ends
+    epilogue32<GATEUP, true, M32>(a, ti, n0, c32, kb, acc);
+}
 
-#pragma unroll
-    for (int mb = 0; mb < M32; ++mb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
-            if (rl >= ti.rows) continue;
-            const size_t orow = (size_t)(ti.row0 + rl);
-            if (GATEUP) {
-                const uint32_t gb = f32_to_bf16_bits(acc[mb][0][i]);
-                const uint32_t ub = f32_to_bf16_bits(acc[mb][1][i]);
-                const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
-                const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
-                store_h<true>(a.out, orow * N, n0 + c32, hb);
-            } else {
-#pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
-                    static_cast<uint16_t*>(a.out)[orow * N + n0 + 32 * cb + c32] =
-                        (uint16_t)f32_to_bf16_bits(acc[mb][cb][i]);
-            }
-        }
-    }
+template <int OP, int M32>
+__global__ __launch_bounds__(256) void k_grouped32_dma(GroupedArgs a) {
+    grouped32_dma_tile<OP, M32>(a);
 }
 
 // Tiles of at most 16 rows (decode): the weights dominate the bytes, so each
@@ -1276,10 +1336,10 @@ __global__ __launch_bounds__(256) void k_grouped_skinny(GroupedArgs a) {
             if (!EXACT) {
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    const uint32_t gb = f32_to_bf16_bits(acc[p][i]);
-                    const uint32_t ub = f32_to_bf16_bits(acc[2 + p][i]);
-                    const uint32_t ab = f32_to_bf16_bits(moe_silu(bf16_bits_to_f32(gb)));
-                    const uint32_t hb = f32_to_bf16_bits(bf16_bits_to_f32(ab) * bf16_bits_to_f32(ub));
+                    const uint32_t v = bf16x2_bits(acc[p][i], acc[2 + p][i]);
+                    const float g = __uint_as_float(v << 16), u = __uint_as_float(v & 0xFFFF0000u);
+                    const uint32_t ab = bf16x2_bits(silu_fast(g), 0.0f) & 0xFFFFu;
+                    const uint32_t hb = bf16x2_bits(__uint_as_float(ab << 16) * u, 0.0f) & 0xFFFFu;
                     if (ok) store_h<F16P>(a.out, orow * N, n0 + 16 * p + r, hb);
                 }
             } else {

@@ -76,6 +76,7 @@ def _declare(L):
     L.oracle_permute.argtypes = [P, I32, I32, I32, P, P, P, P]
     L.oracle_experts_bf16.argtypes = [P, P, I32, I32, I32] + [P] * 6 + [P] * 4
     L.oracle_combine_bf16.argtypes = [P, P, P, I32, I32, I32, P]
+    L.oracle_silu_mul_bf16.argtypes = [P, P, ctypes.c_long, P]
     L.oracle_linear_bf16.argtypes = [P, P, P, I32, I32, I32, P]
     L.oracle_dense_swiglu_bf16.argtypes = [P, P, P, P, I32, I32, I32, P, P]
     L.oracle_rmsnorm_bf16.argtypes = [P, P, F32, I32, I32, P]
@@ -101,7 +102,8 @@ def _declare(L):
                "oracle_quant_f32_int8", "oracle_quant_act_int8", "oracle_group_sums",
                "oracle_exact_linear", "oracle_experts_exact", "oracle_combine_f32",
                "oracle_topk_grouped_from_scores", "oracle_quant_act_int16", "oracle_group_sums16",
-               "oracle_exact_linear16", "oracle_experts_exact16", "oracle_exact_linear_i8w"):
+               "oracle_exact_linear16", "oracle_experts_exact16", "oracle_exact_linear_i8w",
+               "oracle_silu_mul_bf16"):
         getattr(L, fn).restype = None
 
 
@@ -284,6 +286,16 @@ def experts_bf16(rows, experts, W, want=("h", "y")):
                               _p(_c(W["wd"], np.uint8)), _p(_c(W["sd"], np.uint16)),
                               _p(out["g"]), _p(out["u"]), _p(out["h"]), _p(out["y"]))
     return {k_: v for k_, v in out.items() if v is not None}
+
+
+def silu_mul_bf16(g, u):
+    """h = bf16(bf16(silu(g)) * u) elementwise on bf16 bit patterns (the SwiGLU join)."""
+    g = _c(g, np.uint16)
+    u = _c(u, np.uint16)
+    assert g.shape == u.shape
+    h = np.empty_like(g)
+    lib().oracle_silu_mul_bf16(_p(g), _p(u), g.size, _p(h))
+    return h
 
 
 def combine_bf16(y, w, shared=None):

@@ -373,6 +373,16 @@ void oracle_experts_bf16(const uint16_t* rows, const int32_t* experts, int P, in
     }
 }
 
+/* The SwiGLU join alone on given bf16 g and u (the same rounding chain as in
+ * oracle_experts_bf16): h = bf16(bf16(silu(g)) * u), n elements. */
+void oracle_silu_mul_bf16(const uint16_t* g, const uint16_t* u, long n, uint16_t* h) {
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < n; ++i) {
+        uint16_t ab = f64_to_bf16(silu_f64((double)bf16_to_f32(g[i])));
+        h[i] = f64_to_bf16((double)bf16_to_f32(ab) * (double)bf16_to_f32(u[i]));
+    }
+}
+
 /* Weighted sum of the selected expert outputs (Kimi K2.5 donor reference,
  * record "Sum the selected expert outputs with their routing weights";
  * Kimi-K3 latent MoE page, Code: moe_infer multiplies the scattered outputs

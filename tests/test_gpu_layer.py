@@ -16,7 +16,26 @@ from tests.gpu_common import (act_bits_bf16, assert_bf16_close, assert_f32_close
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {1: None, 2: None, 3: 24, 4: 16, 5: 24}
+SAMPLE = {1: None, 2: None, 3: 128, 4: 128, 5: 128}
+
+
+def _sample_tokens(cfg, ridx, n):
+    """n tokens: the seeded sample, plus the tokens of the hottest expert's sorted rows on
+    both sides of every boundary of balanced tiles of 16 to 192 rows (the first and last
+    rows of the grouped kernels' tiles, whichever height they chose)."""
+    T, k, E = cfg["T"], cfg["k"], cfg["E"]
+    counts, offsets, ss, _ = oracle.permute(ridx, E)
+    e = int(np.argmax(counts))
+    cnt, off = int(counts[e]), int(offsets[e])
+    pos = {off, off + cnt - 1}
+    for bm in (16, 32, 48, 64, 96, 128, 192):
+        nt = -(-cnt // bm)
+        rpt = -(-cnt // nt)
+        for t in range(1, min(nt, 4)):
+            pos.update({off + t * rpt - 1, off + t * rpt})
+    edge = {int(ss[p]) // k for p in pos if off <= p < off + cnt}
+    rest = synthetic.token_sample(cfg, max(0, n - len(edge)))
+    return np.array(sorted(edge | set(int(t) for t in rest)), dtype=np.int64)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -56,7 +75,7 @@ def test_layer_parity(cfg_id):
         assert rc[dead].sum() == 0 and dead.sum() == round(0.2 * E)
     # outputs on all tokens or a sample
     n = SAMPLE[cfg_id]
-    toks = np.arange(T) if n is None else synthetic.token_sample(cfg, n)
+    toks = np.arange(T) if n is None else _sample_tokens(cfg, ridx, n)
     say(f"oracle on {len(toks)} tokens of workload {cfg_id}")
     ref, inter = oracle.layer_tokens(inp, toks, topk_idx=ridx, topk_w=rw, want_intermediates=True)
     slots = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)

@@ -170,3 +170,20 @@ def test_latent_and_layer_shapes_match_the_pages():
     for cid in (2, 3, 4, 5):
         c = synthetic.WORKLOADS[cid]
         assert (c["E"], c["k"], c["H"]) == (shp["routed_experts"], shp["experts_per_token"], shp["hidden"])
+
+
+def test_silu_mul_join_against_library_rounding():
+    """The SwiGLU join h = bf16(bf16(silu(g)) * u) on given bf16 g, u: fp64 SiLU from
+    numpy's exp and torch's bf16 rounding; and the join the expert chain takes."""
+    g = np.random.default_rng(40)
+    gg = refmath.bf16_from_f32((g.standard_normal(50000) * 3).astype(np.float32))
+    uu = refmath.bf16_from_f32((g.standard_normal(50000) * 3).astype(np.float32))
+    got = oracle.silu_mul_bf16(gg, uu)
+    a = refmath.bf16_from_f64(refmath.silu64(refmath.bf16_to_f32(gg)))
+    ref = refmath.bf16_from_f64(refmath.bf16_to_f32(a).astype(np.float64) * refmath.bf16_to_f32(uu))
+    np.testing.assert_array_equal(got, ref)
+    # the expert chain's h is the join of its own g and u
+    inp = synthetic.make_inputs(1)
+    rows = inp["x"][:8]
+    r = oracle.experts_bf16(rows, np.arange(8, dtype=np.int32) % 16, inp["experts"], want=("g", "u", "h"))
+    np.testing.assert_array_equal(r["h"], oracle.silu_mul_bf16(r["g"], r["u"]))
