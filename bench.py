@@ -53,12 +53,20 @@ def parse():
                          "report it under 'prefill' (default: on for the default decode workload)")
     ap.add_argument("--no-prefill-leg", dest="prefill_leg", action="store_false")
     ap.add_argument("--no-hbm-probe", action="store_true", help="skip the streaming read and copy probes")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="also time torch's dense bf16 GEMM (hipBLASLt) at the prefill gate/up and down shapes, "
+                         "a practical matrix-core reference under this part's clock behaviour")
     ap.add_argument("--json-out", metavar="PATH", help="also write the JSON line to PATH")
     ap.add_argument("--stats-from", metavar="DIR",
                     help="no run: summarise a rocprofv3 --kernel-trace --stats folder of a bench run (whose line "
                          "--bench-json names) into profiles/moe_layer_<workload>_kernel_stats.md")
     ap.add_argument("--bench-json", metavar="PATH", help="the --json-out file of the profiled run (for --stats-from)")
-    ap.add_argument("--profile-cmd", metavar="CMD", help="the profiled command, quoted in the summary (--stats-from)")
+    ap.add_argument("--profile-cmd", metavar="CMD", action="append",
+                    help="a profiled command, quoted in the summary (--stats-from, --counters-from; repeatable)")
+    ap.add_argument("--counters-from", metavar="DIR", nargs="+",
+                    help="no run: summarise rocprofv3 --pmc folders (one per counter pass) of one workload into "
+                         "profiles/moe_layer_<workload>_counters.md (per-dispatch means and derived rates)")
+    ap.add_argument("--kernel-regex", default="k_grouped", help="kernels kept by --counters-from")
     return ap.parse_args()
 
 
@@ -274,6 +282,32 @@ def hbm_probe():
             "method": "best of 5: 16-byte grid-strided loads over 4 GiB (4096 workgroups); torch copy of 2 GiB"}
 
 
+def gemm_reference():
+    """torch's dense bf16 GEMM (hipBLASLt) at the total shapes of the prefill grouped
+    calls without grouping or int4 (65536 x 4096 x 7168 and 65536 x 7168 x 2048):
+    a practical reference for the matrix-core fraction this part sustains."""
+    import torch
+    out = {}
+    for name, (M, N, K) in (("gate_up_shape", (65536, 4096, 7168)), ("down_shape", (65536, 7168, 2048))):
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            c = a @ b.t()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            c = a @ b.t()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        tf = 2.0 * M * N * K / (ms / 1e3) / 1e12
+        out[name] = {"M": M, "N": N, "K": K, "ms": ms, "TFLOPs": tf, "frac_of_peak": tf / MFMA_F16_PEAK_TFS}
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -322,7 +356,7 @@ def stats_summary(args):
     ks = run["kernel_steps"]
     out = [f"# Layer kernels, workload {cfg_name}", "",
            "Command (on the MI355X, from the repository root), then the summary:", "", "```",
-           args.profile_cmd or "(not given)",
+           *(args.profile_cmd or ["(not given)"]),
            f"python3 bench.py --stats-from {args.stats_from} --bench-json {args.bench_json}", "```", "",
            f"The run made {n_fwd} forwards: {run['warmup']} warmup, {run['steps']} timed (the shared expert on its "
            f"own stream from {run['side_stream_min_t']} tokens), then {ks} per-call event steps with every call alone "
@@ -350,6 +384,71 @@ def stats_summary(args):
     print(f"wrote {path}")
 
 
+SIMDS = 1024          # 256 CUs x 4 SIMDs
+SQ_INSTANCES = 32     # SQ_BUSY_CYCLES is summed over the shader engines (8 XCDs x 4)
+
+
+def counters_summary(args, cfg):
+    """profiles/moe_layer_<workload>_counters.md: per-kernel means per dispatch of every
+    counter in the given rocprofv3 --pmc folders, and the rates derived from them."""
+    import csv
+    import glob
+    import re
+    vals = {}
+    for d in args.counters_from:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name = re.sub(r"\(.*$", "", r["Kernel_Name"].replace("(anonymous namespace)::", ""))
+                name = re.sub(r"^void ", "", name)
+                if not re.search(args.kernel_regex, name):
+                    continue
+                key = (d, r["Dispatch_Id"])
+                v = vals.setdefault(name, {}).setdefault(r["Counter_Name"], {})
+                v[key] = v.get(key, 0.0) + float(r["Counter_Value"])
+    # kernel durations of the counted runs: the bench lines in each folder's log, if kept beside it
+    out = [f"# Counters of the grouped kernels, workload {cfg['name']}", "",
+           "Commands (on the MI355X, from the repository root; one counter pass each), then the summary:", "", "```"]
+    out += list(args.profile_cmd or ["(not given)"])
+    out += [f"python3 bench.py --workload {cfg['id']} --counters-from {' '.join(args.counters_from)}"
+            f" --kernel-regex '{args.kernel_regex}'", "```", "",
+            "Per-dispatch means over every dispatch of the kernel in the run. Derived rates, with the "
+            f"normalisations used: per-SIMD busy cycles = SQ_BUSY_CYCLES / {SQ_INSTANCES} (the counter sums its "
+            f"{SQ_INSTANCES} shader-engine instances); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / {SIMDS} SIMDs / "
+            "per-SIMD busy cycles (SQ_VALU_MFMA_BUSY_CYCLES adds 32 per 32x32x16 and 16 per 16x16x32 operation); "
+            f"VALU busy = 4 SQ_ACTIVE_INST_VALU / {SIMDS} / per-SIMD busy cycles (quad-cycle units); co-issue = "
+            f"SQ_VALU_MFMA_COEXEC_CYCLES / {SIMDS} / per-SIMD busy cycles.", ""]
+    kms = {}
+    if args.bench_json:  # per-call event times of a bench run (the clock estimate below)
+        kms = json.loads(open(args.bench_json).read().strip().splitlines()[-1]).get("kernel_ms", {})
+    for name, cs in sorted(vals.items()):
+        m = {c: float(np.mean(list(v.values()))) for c, v in cs.items()}
+        mo = re.search(r"k_grouped(?:_skinny|_exact)?<(\d+), (\d+)", name) or re.search(r"k_grouped32(?:_dma)?<()(\d+),", name)
+        call = None if not mo else ("moe_int4_grouped_swiglu" if mo.group(2) == "0" else "moe_int4_grouped_down")
+        out += [f"## `{name}`", "", "| counter | mean per dispatch |", "|---|---|"]
+        out += [f"| {c} | {m[c]:.4g} |" for c in sorted(m)]
+        busy = m.get("SQ_BUSY_CYCLES", 0) / SQ_INSTANCES
+        if busy > 0:
+            rates = []
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                rates.append(f"MFMA busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / SIMDS / busy:.1f}%")
+            if "SQ_ACTIVE_INST_VALU" in m:
+                rates.append(f"VALU busy {100 * 4 * m['SQ_ACTIVE_INST_VALU'] / SIMDS / busy:.1f}%")
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+                rates.append(f"VALU and MFMA together {100 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / SIMDS / busy:.1f}%")
+            if "SQ_INSTS_VALU" in m and "SQ_INSTS_MFMA" in m and m["SQ_INSTS_MFMA"] > 0:
+                rates.append(f"non-MFMA VALU instructions per MFMA "
+                             f"{(m['SQ_INSTS_VALU'] - m['SQ_INSTS_MFMA']) / m['SQ_INSTS_MFMA']:.2f}")
+            if call in kms:
+                rates.append(f"clock about {busy / (kms[call] * 1e-3) / 1e9:.2f} GHz (per-SIMD busy cycles over "
+                             f"{kms[call]:.3f} ms, the {call} event time of the --bench-json run)")
+            out += ["", f"Per-SIMD busy cycles per dispatch: {busy:.4g}. " + "; ".join(rates) + "."]
+        out.append("")
+    path = os.path.join(ROOT, "profiles", f"moe_layer_{cfg['name']}_counters.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out))
+    print(f"wrote {path}")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -362,6 +461,9 @@ def main():
         if not args.calibrate_copy:
             sys.exit("--traffic-from needs --calibrate-copy MIB, the copy size of the counted run")
         write_traffic(args, cfg0)
+        return
+    if args.counters_from:
+        counters_summary(args, cfg0)
         return
     if args.stats_from:
         if not args.bench_json:
@@ -462,6 +564,8 @@ def main():
 
     if not args.no_hbm_probe:
         line["hbm_probe"] = hbm_probe()
+    if args.gemm_reference:
+        line["gemm_reference"] = gemm_reference()
 
     if not args.no_cpu_baseline:
         import oracle

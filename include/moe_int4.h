@@ -174,14 +174,17 @@ int moe_quant_act_int16(const uint16_t* x, int M, int K, int16_t* q, float* s, v
  * Weight fragment layout for the grouped GEMMs (a layout step of this library,
  * not of the method: the checkpoint buffers of "Kimi exact-generator
  * adaptation", "The proposed substitution", load without any arithmetic
- * conversion; this reorders their bytes once, exactly).
+ * conversion; this reorders their bytes once, exactly, and stores the scales
+ * as fp16, the operand format of the dequantisation, which is exact for the
+ * scales moe_int4_check_scales accepts).
  * Input: a stacked expert matrix in the checkpoint layout, packed [E][N][K/2],
  * scale [E][N][K/32] bf16.  Output (same sizes, out of place): with
  * nch = K/128, row group R = e*(N/16) + n/16 and chunk c,
  *   packed_out[((R*nch + c)*64 + l)*16 + 4g + b] = packed[row 16(R%(N/16))+r of
  *       expert e][64c + 16g + 4j + b],  lane l = r + 16j (r < 16, j < 4),
  *       g < 4, b < 4   (1 KB per (R, c): 16 rows x 128 K, lane-major)
- *   scale_out[((R*nch + c)*16 + r)*4 + g] = scale[row ...][4c + g]
+ *   scale_out[((R*nch + c)*16 + r)*4 + g] = fp16(scale[row ...][4c + g])
+ *       (fp16 bits; bf16 -> fp16 rounds to nearest even)
  * Nibble order inside each byte is unchanged.  N a multiple of 16, K of 128;
  * packed buffers 16-byte and scale buffers 8-byte aligned; input and output
  * must not overlap.  E == 0 is a no-op. */
@@ -237,7 +240,7 @@ int moe_act_f16p(const uint16_t* x, int rows, int K, uint16_t* out, void* stream
  *     staging format of the bf16 h that MOE_MODE_BF16 writes).  Results are
  *     bit-identical to MOE_MODE_BF16; the kernels skip the per-tile
  *     conversion of the activations.
- * gate/up weights in the fragment layout of moe_int4_prepack.
+ * gate/up weights and their fp16 scales in the fragment layout of moe_int4_prepack.
  * Empty experts are skipped; rows of absent experts are not written. */
 int moe_int4_grouped_swiglu(int mode, const void* act, const float* act_scale,
                             const uint8_t* gate_packed, const uint16_t* gate_scale,
@@ -255,7 +258,7 @@ int moe_int4_grouped_swiglu(int mode, const void* act, const float* act_scale,
  *   MOE_MODE_BF16_F16P: h in the fp16 staging format (as written by
  *     moe_int4_grouped_swiglu in that mode) -> y [T*k, H] bf16, bit-identical
  *     to MOE_MODE_BF16 on the bf16 h. 
- * down weights in the fragment layout of moe_int4_prepack. */
+ * down weights and their fp16 scales in the fragment layout of moe_int4_prepack. */
 int moe_int4_grouped_down(int mode, const void* h, const float* h_scale, const uint8_t* down_packed,
                           const uint16_t* down_scale, const int32_t* offsets, int T, int k, int E,
                           int I, int H, void* y, void* stream);

@@ -207,15 +207,13 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, half2_t s2, half2_t
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, (sh & M) ^ X), s2, c2));
 }
 
-// bf16 scale bits -> (s, s) and (-24 s, -24 s) in fp16.
+// Group scale (fp16 bits, as moe_int4_prepack stores it) -> (s, s) and
+// (-24 s, -24 s) in fp16; -24 s is exact for scales in the supported range.
 __device__ __forceinline__ void scale_pair(uint32_t sbits, half2_t& s2, half2_t& c2) {
-    const float s = bf16_bits_to_f32(sbits & 0xFFFFu);
-    const _Float16 sh = (_Float16)s;
-    const _Float16 ch = (_Float16)(-24.0f * s);
-    s2 = half2_t{sh, sh};
-    c2 = half2_t{ch, ch};
+    const uint32_t b = sbits & 0xFFFFu;
+    s2 = __builtin_bit_cast(half2_t, b | (b << 16));
+    c2 = s2 * half2_t{(_Float16)-24.0f, (_Float16)-24.0f};
 }
-
 // 8 bf16 (4 dwords, elements in order) -> 8 fp16 in the (p, p+4) pair order.
 __device__ __forceinline__ u32x4_t bf16x8_to_f16_perm(u32x4_t d) {
     const float f0 = __uint_as_float(d[0] << 16), f1 = __uint_as_float(d[0] & 0xFFFF0000u);
@@ -1395,7 +1393,8 @@ __global__ __launch_bounds__(256) void k_prepack_w(const uint8_t* __restrict__ s
     *reinterpret_cast<u32x4_t*>(dst + (size_t)t * 16) = v;
 }
 
-// One thread per (fragment, row): the row's 4 group scales of the chunk.
+// One thread per (fragment, row): the row's 4 group scales of the chunk, converted
+// to fp16 (the operand format of the dequantisation).
 __global__ __launch_bounds__(256) void k_prepack_s(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                                                   long pieces, int K) {
     const long t = (long)blockIdx.x * 256 + threadIdx.x;
@@ -1406,7 +1405,15 @@ __global__ __launch_bounds__(256) void k_prepack_s(const uint16_t* __restrict__ 
     const long rg = fid / nch;
     const int c = (int)(fid % nch);
     const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src + (size_t)(rg * 16 + r) * (size_t)(K / 32) + 4 * c);
-    *reinterpret_cast<u32x2_t*>(dst + (size_t)t * 4) = v;
+    // bf16 -> fp16 (round to nearest even; exact for the scales moe_int4_check_scales accepts)
+    u32x2_t o;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const _Float16 lo = (_Float16)bf16_bits_to_f32(v[h] & 0xFFFFu);
+        const _Float16 hi = (_Float16)bf16_bits_to_f32(v[h] >> 16);
+        o[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *reinterpret_cast<u32x2_t*>(dst + (size_t)t * 4) = o;
 }
 
 // Scale range check: a bf16 scale keeps the fp16 dequantisation exact when it

@@ -28,7 +28,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace moe
 
-extern "C" int moe_abi_version(void) { return 3; }
+extern "C" int moe_abi_version(void) { return 4; }
 
 extern "C" const char* moe_status_string(int status) {
     switch (status) {

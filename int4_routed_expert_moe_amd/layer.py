@@ -31,10 +31,10 @@ def _u8(a: np.ndarray, device) -> torch.Tensor:
 
 def prepack_experts(ex: dict) -> dict:
     """Checkpoint-layout expert tensors (wg/sg, wu/su, wd/sd) -> the fragment layout
-    the grouped GEMMs read (one exact byte permutation per matrix, on the GPU)."""
+    the grouped GEMMs read (one exact byte permutation per matrix, scales as fp16, on the GPU)."""
     out = {}
     for w, s in (("wg", "sg"), ("wu", "su"), ("wd", "sd")):
-        pw, ps = torch.empty_like(ex[w]), torch.empty_like(ex[s])
+        pw, ps = torch.empty_like(ex[w]), torch.empty_like(ex[s], dtype=torch.float16)
         _m.moe_int4_prepack(ex[w], ex[s], pw, ps)
         out[w], out[s] = pw, ps
     return out
@@ -49,8 +49,9 @@ class MoELayer:
 
     SIDE_STREAM_MIN_T = 64  # tokens from which the shared expert runs on its own stream
     # tokens from which the bf16 expert input is converted once to the fp16 staging
-    # format (instead of by every tile of the grouped GEMMs)
-    STAGED_ACT_MIN_T = 256
+    # format instead of by every tile of the grouped GEMMs: always (the decode kernel
+    # then skips its per-wave conversion, measured 3.9% faster at 64 tokens)
+    STAGED_ACT_MIN_T = 1
 
     def __init__(self, cfg: dict, router_w, router_b, experts: dict, shared: dict | None = None,
                  latent: dict | None = None):

@@ -194,8 +194,9 @@ def moe_exact_linear_i8w(qx, sx, qw, sw, y):
 
 
 def moe_int4_prepack(packed, scale, packed_out, scale_out):
-    """Checkpoint-layout expert matrices [E, N, K/2] + [E, N, K/32] -> the fragment layout
-    the grouped GEMMs read (same shapes and dtypes, out of place)."""
+    """Checkpoint-layout expert matrices [E, N, K/2] uint8 + [E, N, K/32] bf16 -> the
+    fragment layout the grouped GEMMs read (same shapes, out of place; the scales
+    come out as fp16)."""
     if packed.dim() != 3:
         raise ValueError("packed must be [E, N, K/2]")
     E, N, K2 = packed.shape
@@ -203,7 +204,7 @@ def moe_int4_prepack(packed, scale, packed_out, scale_out):
     _need(packed, torch.uint8, (E, N, K // 2), "packed")
     _need(scale, torch.bfloat16, (E, N, K // 32), "scale")
     _need(packed_out, torch.uint8, (E, N, K // 2), "packed_out")
-    _need(scale_out, torch.bfloat16, (E, N, K // 32), "scale_out")
+    _need(scale_out, torch.float16, (E, N, K // 32), "scale_out")
     _check("moe_int4_prepack", _lib.moe_int4_prepack(_ptr(packed), _ptr(scale), E, N, K, _ptr(packed_out),
                                                      _ptr(scale_out), _stream()))
 
@@ -238,9 +239,9 @@ def moe_int4_grouped_swiglu(mode, act, act_scale, gate_packed, gate_scale, up_pa
                             sorted_slot, T, k, E, H, I, h, h_scale):
     _need(act, _ACT_DTYPE.get(mode, torch.bfloat16), (T, H), "act")
     for t, dt, shp, nm in ((gate_packed, torch.uint8, (E, I, H // 2), "gate_packed"),
-                           (gate_scale, torch.bfloat16, (E, I, H // 32), "gate_scale"),
+                           (gate_scale, torch.float16, (E, I, H // 32), "gate_scale"),
                            (up_packed, torch.uint8, (E, I, H // 2), "up_packed"),
-                           (up_scale, torch.bfloat16, (E, I, H // 32), "up_scale"),
+                           (up_scale, torch.float16, (E, I, H // 32), "up_scale"),
                            (offsets, torch.int32, (E + 1,), "offsets"),
                            (sorted_slot, torch.int32, (T * k,), "sorted_slot")):
         _need(t, dt, shp, nm)
@@ -258,7 +259,7 @@ def moe_int4_grouped_swiglu(mode, act, act_scale, gate_packed, gate_scale, up_pa
 def moe_int4_grouped_down(mode, h, h_scale, down_packed, down_scale, offsets, T, k, E, I, H, y):
     _need(h, _ACT_DTYPE.get(mode, torch.bfloat16), (T * k, I), "h")
     _need(down_packed, torch.uint8, (E, H, I // 2), "down_packed")
-    _need(down_scale, torch.bfloat16, (E, H, I // 32), "down_scale")
+    _need(down_scale, torch.float16, (E, H, I // 32), "down_scale")
     _need(offsets, torch.int32, (E + 1,), "offsets")
     if mode not in _EXACT_MODES:
         _need(y, torch.bfloat16, (T * k, H), "y")
