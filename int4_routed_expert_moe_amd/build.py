@@ -46,19 +46,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+# host-side sanitizers for the argument checks (the device code is built as usual)
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, objdir: str = OBJDIR, extra=()) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def _link(objs, out):
+def _link(objs, out, extra=()):
     tmp = out + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -80,6 +85,22 @@ def build(verbose: bool = True) -> str:
     return OUT
 
 
+def build_sanitized(verbose: bool = True) -> str:
+    """libmoe_int4_san.so: the same sources with the host code under AddressSanitizer and
+    UndefinedBehaviorSanitizer, for the CPU-side argument checks (load it with clang's
+    ASan runtime preloaded; no GPU is needed for the checks)."""
+    objdir = os.path.join(OBJDIR, "san")
+    os.makedirs(objdir, exist_ok=True)
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda src: _compile(src, objdir, SAN_FLAGS), SOURCES))
+    out = os.path.join(HERE, "libmoe_int4_san.so")
+    _link(objs, out, ["-fsanitize=address,undefined"])
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
-    build()
+    build_sanitized() if "--sanitize" in sys.argv else build()
     sys.exit(0)

@@ -26,13 +26,21 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_LIB selects another build of the same source (the sanitizer build below)
+_LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "libmoe_oracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+SAN_FLAGS = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc into oracle/libmoe_oracle.so."""
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc into oracle/libmoe_oracle.so, or with AddressSanitizer and
+    UndefinedBehaviorSanitizer into oracle/libmoe_oracle_san.so (load it with MOE_ORACLE_LIB and
+    gcc's libasan/libubsan preloaded)."""
+    if sanitize:
+        out = os.path.join(_HERE, "libmoe_oracle_san.so")
+        subprocess.check_call(["gcc", *CFLAGS, *SAN_FLAGS, _SRC, "-o", out, "-lm"])
+        return out
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])

@@ -8,7 +8,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_int4.h")
-LIB = os.path.join(ROOT, "int4_routed_expert_moe_amd", "libmoe_int4.so")
+# MOE_LIB selects another build of the library (the host-sanitizer build)
+LIB = os.environ.get("MOE_LIB") or os.path.join(ROOT, "int4_routed_expert_moe_amd", "libmoe_int4.so")
 
 
 @pytest.fixture(scope="module")
