@@ -86,6 +86,8 @@ const char* moe_last_error_detail(void);
  *   topk_w[t,j] = s_sel / (sum_j s_sel + 1e-20)  (renormalize != 0; else s_sel)
  * x [T,H] bf16; w_router [E,H] bf16; bias [E] fp32;
  * out: topk_idx [T,k] int32, topk_w [T,k] fp32.
+ * H a multiple of 64, k <= min(E, 16), E <= 1024, E*H*2 bytes below 4 GiB
+ * (else MOE_ERR_UNSUPPORTED).
  * ws: device workspace of at least moe_route_workspace_bytes(T, H, E) bytes,
  * 16-byte aligned (it holds the fp32 logits and, for up to 256 tokens, the
  * 64-wide block sums).

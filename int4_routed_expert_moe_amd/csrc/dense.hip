@@ -54,14 +54,6 @@ __device__ __forceinline__ uint32_t add_bits(uint32_t yb, uint16_t addv) {
     return f32_to_bf16_bits(bf16_bits_to_f32(yb) + bf16_bits_to_f32(addv));
 }
 
-// Workgroup barrier for LDS traffic only (waits for this wave's LDS operations,
-// not its global loads, so the weight prefetch survives it).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Column layout of a wave (CB blocks of 16 columns):
 //   linear: output columns n0 + 16 cb + r, n0 = chunk * 64 CB + wave * 16 CB
 //   swiglu: blocks [0, CB/2) gate, [CB/2, CB) up, same output columns

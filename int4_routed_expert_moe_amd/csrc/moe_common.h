@@ -51,6 +51,55 @@ __device__ __forceinline__ long xcd_logical_block(int per_xcd) {
     return (b & 7) * (long)per_xcd + (b >> 3);
 }
 
+// Descriptor for raw buffer loads from `bytes` bytes at p (gfx9 family: the
+// fourth word selects the 32-bit data format).  Offsets are 32-bit, and loads
+// past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// The same for an address and size that are wave-uniform but computed from
+// values the compiler cannot prove uniform: both are read from the first lane
+// (a descriptor it took for divergent would be used through a loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_uniform(const void* p, uint32_t bytes) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return buffer_rsrc(reinterpret_cast<const void*>(lo | (hi << 32)), (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt) but not for its global loads, so prefetched weights and the next
+// activation chunk stay in flight across it (a full __syncthreads also drains
+// every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One 16-byte buffer load per lane written straight to LDS: lane l's bytes go
+// to lds + 16 l (lds wave-uniform).  The builtin exists for the device pass
+// only; the host pass compiles the kernels' launch stubs.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, uint32_t voffset,
+                                                  uint32_t soffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                             voffset, soffset, 0, 0);
+#else
+    (void)rsrc, (void)lds, (void)voffset, (void)soffset;
+#endif
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order).  Used where the compiler cannot see the wait:
+// LDS written by global-to-LDS loads, read by other waves after a barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // e^t for the router's sigmoid and SiLU: Cody-Waite reduction t = n ln2 + r
 // with n = rint(t log2 e) and a two-part ln2, the degree-7 Taylor polynomial
 // of e^r by Horner's rule with fused multiply-adds, then scaling by 2^n

@@ -7,22 +7,18 @@
 //
 // The selected indices must be reproducible bit for bit, so every logit is
 // summed in one fixed fp32 order: each 64-element hidden block from 0 in
-// ascending index, then the block sums from 0 in ascending block order (no
-// matrix cores: their internal summation order is unspecified).
+// ascending index, then the block sums from 0 in ascending block order.  Few
+// tokens: fma chains on the VALU; many: the fp32 matrix-core shape with K = 1,
+// which adds one product per step with one rounding (no multi-term sums).
 #include "moe_common.h"
+
+#include <algorithm>
 
 namespace {
 
 constexpr int kRouteTok = 64;   // tokens per block
 constexpr int kRouteKC = 64;    // hidden elements per block sum (one LDS chunk)
-
-// Workgroup barrier for LDS traffic only (the next tiles' global loads stay in
-// flight across it).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+constexpr int kRouterWaves = 4; // waves (16 experts each) per many-token logits workgroup
 
 // Stage 64 rows x 64 hidden elements of a bf16 matrix as fp32, transposed to
 // [i][row]; rows at or past `limit` are zero.  Two 16-byte pieces per thread.
@@ -57,67 +53,6 @@ __device__ __forceinline__ void tile_store(const TileLoad& tl, float (*dst)[64 +
     }
 }
 
-// Stage R = 16*CE rows x 64 hidden elements of the router matrix as fp32,
-// transposed to [i][slot], where row r sits in slot 4*(r / CE) + r % CE (so a
-// thread's CE rows are one 16-byte LDS read); rows at or past `limit` are zero.
-template <int CE>
-struct WTileLoad {
-    static constexpr int R = 16 * CE;
-    static constexpr int IT = (R * 8 + 255) / 256;  // 16-byte pieces per thread
-    u32x4_t v[IT];
-};
-template <int CE>
-__device__ __forceinline__ void wtile_load(WTileLoad<CE>& tl, const uint16_t* __restrict__ m, int row0, int limit,
-                                           int H, int col0) {
-    constexpr int R = WTileLoad<CE>::R;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int it = 0; it < WTileLoad<CE>::IT; ++it) {
-        const int p = it * 256 + tid;
-        const int row = p % R, piece = p / R;  // consecutive lanes: consecutive rows of one piece
-        const bool ok = p < R * 8 && row0 + row < limit;
-        tl.v[it] = *reinterpret_cast<const u32x4_t*>(m + (size_t)(ok ? row0 + row : 0) * H + col0 + piece * 8);
-        if (!ok) tl.v[it] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-}
-template <int CE>
-__device__ __forceinline__ void wtile_store(const WTileLoad<CE>& tl, float (*dst)[64 + 4]) {
-    constexpr int R = WTileLoad<CE>::R;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int it = 0; it < WTileLoad<CE>::IT; ++it) {
-        const int p = it * 256 + tid;
-        if (p >= R * 8) continue;
-        const int row = p % R, piece = p / R;
-        const int slot = 4 * (row / CE) + row % CE;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            dst[piece * 8 + 2 * j][slot] = __uint_as_float(tl.v[it][j] << 16);
-            dst[piece * 8 + 2 * j + 1][slot] = __uint_as_float(tl.v[it][j] & 0xFFFF0000u);
-        }
-    }
-}
-
-// One 64-long ascending chain per (token, expert) of a 4 x CE register tile
-// (experts in the slot layout of wtile_store).
-template <int CE>
-__device__ __forceinline__ void block_chain_ce(const float (*xs)[64 + 4], const float (*ws)[64 + 4], int tt, int te,
-                                               float (&acc)[4][CE]) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < CE; ++c) acc[a][c] = 0.0f;
-#pragma unroll 4
-    for (int i = 0; i < kRouteKC; ++i) {
-        const f32x4_t xv = *reinterpret_cast<const f32x4_t*>(&xs[i][4 * tt]);
-        const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(&ws[i][4 * te]);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int c = 0; c < CE; ++c) acc[a][c] = __builtin_fmaf(xv[a], wv[c], acc[a][c]);
-    }
-}
-
 // One 64-long ascending chain per (token, expert) of a 4x4 register tile.
 __device__ __forceinline__ void block_chain(const float (*xs)[64 + 4], const float (*ws)[64 + 4], int tt, int te,
                                             float (&acc)[4][4]) {
@@ -136,58 +71,123 @@ __device__ __forceinline__ void block_chain(const float (*xs)[64 + 4], const flo
     }
 }
 
-// Logits of 64 tokens x 64 experts for many tokens: each thread owns 4 tokens x
-// 4 experts; per 64-wide hidden block it forms the block sums (ascending chain)
-// and adds them to its running totals in ascending block order.  x and router
-// tiles are staged in LDS as fp32, double buffered: the next block's loads are
-// in flight during the current block's chains (one LDS-only barrier per block).
-// Grid: (ceil(E/64), ceil(T/64)).
-template <int CE>
-__global__ __launch_bounds__(256) void k_router_full(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-                                                     int T, int H, int E, float* __restrict__ logits) {
-    constexpr int R = 16 * CE;  // experts per block
-    __shared__ __attribute__((aligned(16))) float xs[2][kRouteKC][64 + 4];  // [i][t]
-    __shared__ __attribute__((aligned(16))) float ws[2][kRouteKC][64 + 4];  // [i][slot]
-    const int tid = threadIdx.x;
-    const int e0 = blockIdx.x * R;
-    const int t0 = blockIdx.y * kRouteTok;
+// Logits on the matrix cores.  The fp32 16x16x1 shape adds one product to
+// each output per instruction with a single rounding, the same as an fma
+// (products of bf16 values are exact in fp32), so a run of them in ascending
+// hidden index is exactly the block chain; the block sums are then added to the
+// running totals in ascending block order on the VALU.  A workgroup of NW waves
+// owns 64 tokens x 16 NW experts; wave w multiplies all 64 tokens (four blocks
+// of 16) by experts e0 + 16w .. e0 + 16w + 15.  Per 64-wide hidden block the
+// token and router tiles go straight from memory to LDS by buffer loads as
+// 16-byte pieces of 8 elements, laid out [piece][row] (tokens: 64 rows; router:
+// 16 NW rows), so that the operand reads are 16 bytes per lane, conflict free.
+// Three tile buffers: block b+2 loads while block b is multiplied, and each wave
+// waits for its own loads of block b+1 before the barrier that ends step b.
+// Lane l feeds token t0 + l and expert e0 + 16w + l mod 16; element i of its
+// result is token t0 + 16(i/4) + 4(l/16) + i mod 4.  Rows past T or E load a
+// valid row and are not stored.  The expert tiles of one token tile run on one
+// XCD.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_router_mfma(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ w, int T, int H, int E,
+                                                         float* __restrict__ logits, int n_et, int per_xcd) {
+    constexpr int RW = 16 * NW;           // router rows per tile
+    constexpr int NI = 8 + RW / 8;        // 1-KB load instructions per block (token tile: 8)
+    static_assert(NI % NW == 0, "load instructions shared evenly by the waves");
+    constexpr int PER = NI / NW;          // this wave's load instructions per block
+    __shared__ __attribute__((aligned(16))) uint16_t X0[8][64][8], X1[8][64][8], X2[8][64][8];
+    __shared__ __attribute__((aligned(16))) uint16_t W0[8][RW][8], W1[8][RW][8], W2[8][RW][8];
+    auto xt = [&](auto bc) -> uint16_t(&)[8][64][8] {
+        if constexpr (decltype(bc)::value == 0) return X0;
+        else if constexpr (decltype(bc)::value == 1) return X1;
+        else return X2;
+    };
+    auto wt = [&](auto bc) -> uint16_t(&)[8][RW][8] {
+        if constexpr (decltype(bc)::value == 0) return W0;
+        else if constexpr (decltype(bc)::value == 1) return W1;
+        else return W2;
+    };
+
+    const long L = xcd_logical_block(per_xcd);
+    const long n_tt = (T + kRouteTok - 1) / kRouteTok;
+    if (L >= n_tt * n_et) return;
+    const int t0 = (int)(L / n_et) * kRouteTok;
+    const int e0 = (int)(L % n_et) * RW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int NB = H / kRouteKC;
-    const int tt = tid >> 4, te = tid & 15;
-    TileLoad lx;
-    WTileLoad<CE> lw;
-    tile_load(lx, x, t0, T, H, 0);
-    wtile_load<CE>(lw, w, e0, E, H, 0);
-    tile_store(lx, xs[0]);
-    wtile_store<CE>(lw, ws[0]);
-    lds_barrier();
-    float total[4][CE];
+
+    // this wave's load instructions j = wave + NW m: j < 8 is piece j of the
+    // token tile (lane l: row l); j >= 8 covers router slots 64 (j - 8) + l of
+    // the [piece][row] layout
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)((size_t)T * H * 2));
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w, (uint32_t)((size_t)E * H * 2));
+    uint32_t voff[PER];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < CE; ++c) total[a][c] = 0.0f;
-    for (int b = 0; b < NB; ++b) {
-        const int buf = b & 1;
-        const int bn = min(b + 1, NB - 1);  // past the end: a redundant in-bounds load, never used
-        tile_load(lx, x, t0, T, H, bn * kRouteKC);
-        wtile_load<CE>(lw, w, e0, E, H, bn * kRouteKC);
-        float acc[4][CE];
-        block_chain_ce<CE>(xs[buf], ws[buf], tt, te, acc);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int c = 0; c < CE; ++c) total[a][c] = total[a][c] + acc[a][c];  // block sums in ascending order
-        tile_store(lx, xs[buf ^ 1]);
-        wtile_store<CE>(lw, ws[buf ^ 1]);
-        lds_barrier();
+    for (int m = 0; m < PER; ++m) {
+        const int j = wave + NW * m;
+        if (j < 8) {
+            voff[m] = ((uint32_t)min(t0 + lane, T - 1) * (uint32_t)H + 8u * (uint32_t)j) * 2u;
+        } else {
+            const int s = 64 * (j - 8) + lane;
+            voff[m] = ((uint32_t)min(e0 + s % RW, E - 1) * (uint32_t)H + 8u * (uint32_t)(s / RW)) * 2u;
+        }
     }
+    auto load_block = [&](int b, auto bc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int t = t0 + 4 * tt + a;
-        if (t >= T) continue;
-        float* dst = logits + (size_t)t * E + e0 + CE * te;
+        for (int m = 0; m < PER; ++m) {
+            const int j = wave + NW * m;
+            if (j < 8) buffer_load_lds16(xr, &xt(bc)[j][0][0], voff[m], (uint32_t)b * (kRouteKC * 2));
+            else buffer_load_lds16(wr, &wt(bc)[0][0][0] + 64 * 8 * (j - 8), voff[m], (uint32_t)b * (kRouteKC * 2));
+        }
+    };
+    auto elem = [](const u32x4_t& v, int q) __attribute__((always_inline)) {
+        return __uint_as_float((q & 1) ? (v[q >> 1] & 0xFFFF0000u) : (v[q >> 1] << 16));
+    };
+    f32x16_t tot = {};
+    // one block: 64 dependent steps from zero, then the block sum into the total
+    auto block = [&](auto bc) __attribute__((always_inline)) {
+        f32x16_t part = {};
 #pragma unroll
-        for (int c = 0; c < CE; ++c)
-            if (e0 + CE * te + c < E) dst[c] = total[a][c];
+        for (int g = 0; g < 8; ++g) {
+            const u32x4_t xa = *reinterpret_cast<const u32x4_t*>(&xt(bc)[g][lane][0]);
+            const u32x4_t wa = *reinterpret_cast<const u32x4_t*>(&wt(bc)[g][16 * wave + (lane & 15)][0]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                part = __builtin_amdgcn_mfma_f32_16x16x1f32(elem(xa, q), elem(wa, q), part, 0, 0, 0);
+        }
+        tot = tot + part;
+    };
+    auto step = [&](auto bc, int b) __attribute__((always_inline)) {
+        constexpr std::integral_constant<int, (decltype(bc)::value + 2) % 3> bn{};
+        load_block(min(b + 2, NB - 1), bn);  // past the end: a redundant in-bounds load, never used
+        block(bc);
+        wait_vmcnt<PER>();  // this wave's loads of block b+1 have landed
+        lds_barrier();
+    };
+    constexpr std::integral_constant<int, 0> B0{};
+    constexpr std::integral_constant<int, 1> B1{};
+    constexpr std::integral_constant<int, 2> B2{};
+    load_block(0, B0);
+    load_block(min(1, NB - 1), B1);
+    wait_vmcnt<PER>();
+    lds_barrier();
+    int b = 0;
+    for (; b + 3 <= NB; b += 3) {
+        step(B0, b);
+        step(B1, b + 1);
+        step(B2, b + 2);
+    }
+    if (b < NB) step(B0, b);
+    if (b + 1 < NB) step(B1, b + 1);
+    wait_vmcnt<0>();  // the trailing redundant loads land before the workgroup ends
+
+    const int ex = e0 + 16 * wave + (lane & 15);
+    if (ex >= E) return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int tok = t0 + 16 * (i >> 2) + 4 * (lane >> 4) + (i & 3);
+        if (tok < T) logits[(size_t)tok * E + ex] = tot[i];
     }
 }
 
@@ -406,6 +406,8 @@ int route_impl(const uint16_t* x, const uint16_t* w_router, const float* bias, i
         return fail(MOE_ERR_UNSUPPORTED, "moe_route: need k <= min(E,16), E <= 1024 (E=%d k=%d)", E, k);
     if (H % kRouteKC != 0)
         return fail(MOE_ERR_UNSUPPORTED, "moe_route: H=%d must be a multiple of %d", H, kRouteKC);
+    if ((size_t)E * (size_t)H * 2 >= ((size_t)1 << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "moe_route: the router matrix (E=%d, H=%d) must stay below 4 GiB", E, H);
     if (T == 0) return MOE_OK;
     if (!x || !w_router || !bias || !topk_idx || !topk_w)
         return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
@@ -427,14 +429,17 @@ int route_impl(const uint16_t* x, const uint16_t* w_router, const float* bias, i
         const long n = (long)T * E;
         hipLaunchKernelGGL(k_router_blocksum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, T, NB, E, logits);
     } else {
-        // 64 or 48 experts per block, whichever fills the CUs more evenly (48:
-        // 8 blocks per 64 tokens at 384 experts)
-        auto fill = [](long n) { return (double)n / (double)(256 * ((n + 255) / 256)); };
-        const long n64 = (long)((E + 63) / 64) * tb, n48 = (long)((E + 47) / 48) * tb;
-        if (fill(n48) > fill(n64))
-            hipLaunchKernelGGL(k_router_full<3>, dim3((E + 47) / 48, tb), dim3(256), 0, st, x, w_router, T, H, E, logits);
-        else
-            hipLaunchKernelGGL(k_router_full<4>, dim3((E + 63) / 64, tb), dim3(256), 0, st, x, w_router, T, H, E, logits);
+        // chunks of tokens whose rows stay below 2 GiB (the kernel's buffer
+        // offsets are 32-bit); 64 experts per workgroup
+        constexpr int NW = kRouterWaves;
+        const long tc = (((1L << 31) - 1) / ((long)H * 2)) / kRouteTok * kRouteTok;
+        const int n_et = (E + 16 * NW - 1) / (16 * NW);
+        for (long c0 = 0; c0 < T; c0 += tc) {
+            const int Tc = (int)std::min<long>(tc, (long)T - c0);
+            const int per_xcd = moe::per_xcd((long)n_et * ((Tc + kRouteTok - 1) / kRouteTok));
+            hipLaunchKernelGGL(k_router_mfma<NW>, dim3(8 * per_xcd), dim3(64 * NW), 0, st, x + (size_t)c0 * H,
+                               w_router, Tc, H, E, logits + (size_t)c0 * E, n_et, per_xcd);
+        }
     }
     int rc = launch_status("moe_route logits");
     if (rc) return rc;

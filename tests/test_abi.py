@@ -65,6 +65,8 @@ def test_host_validation_rejects_bad_arguments(lib):
     assert _status(lib, "moe_route", fake, fake, fake, 4, 256, 8, 9, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -2
     assert _status(lib, "moe_route", fake, fake, fake, 4, 256, 2000, 8, 1, fake, fake, fake, ctypes.c_size_t(1 << 30), null) == -2
     assert _status(lib, "moe_route", fake, fake, fake, 4, 200, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -2
+    # a router matrix of 4 GiB (1024 experts x 2^21 hidden, bf16) is past the kernel's 32-bit offsets
+    assert _status(lib, "moe_route", fake, fake, fake, 4, 1 << 21, 1024, 2, 1, fake, fake, fake, ctypes.c_size_t(1 << 30), null) == -2
     assert _status(lib, "moe_route", null, fake, fake, 4, 256, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -1
     assert _status(lib, "moe_route", odd, fake, fake, 4, 256, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(1 << 20), null) == -1
     assert _status(lib, "moe_route", fake, fake, fake, 4, 256, 16, 2, 1, fake, fake, fake, ctypes.c_size_t(8), null) == -3

@@ -52,8 +52,11 @@ def _scales(g, shape):
 @pytest.mark.parametrize("T,H,E,k,seed", [
     (1, 128, 16, 1, 0), (37, 256, 16, 2, 1), (64, 7168, 384, 8, 2), (300, 1024, 384, 8, 3),
     (130, 512, 1000, 16, 4), (64, 256, 8, 8, 5),
-    (300, 512, 100, 4, 6),      # large-batch path, 48-expert blocks, ragged last block
-    (8192, 128, 384, 8, 7),     # large-batch path, 64-expert blocks
+    (300, 512, 100, 4, 6),      # large-batch path, ragged last expert tile
+    (8192, 128, 384, 8, 7),     # large-batch path, two hidden blocks
+    (300, 64, 50, 4, 8),        # large-batch path, one hidden block, ragged tokens and experts
+    (260, 320, 70, 6, 9),       # large-batch path, five hidden blocks (loop plus both tail steps)
+    (2048, 7168, 384, 8, 10),   # large-batch path at the full hidden size
 ])
 def test_route_bitexact(m, T, H, E, k, seed):
     say(f"route T={T} H={H} E={E} k={k}")
@@ -304,6 +307,10 @@ def _routing(g, T, E, k, skew=False):
     (280, 256, 128, 8, 2, False, 4),     # 6-block tiles
     (400, 512, 256, 8, 2, True, 5),      # 8-block tiles, skewed
     (700, 256, 128, 6, 2, False, 6),     # 32x32 tiles over 2 K chunks (gate/up) and 1 (down)
+    # several column chunks per staged item, the load ring running across them:
+    (700, 1024, 512, 6, 2, False, 7),    # gate/up 8 K chunks, 2 per item; down 4 K chunks, 4 per item
+    (500, 1536, 384, 5, 2, True, 8),     # gate/up 1 per item; down 3 K chunks (the least), 2 per item
+    (700, 1280, 512, 6, 2, False, 9),    # gate/up 10 K chunks, 2 per item; down 1 per item
 ])
 def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     say(f"grouped bf16 T={T} H={H} I={I} E={E} k={k}")
