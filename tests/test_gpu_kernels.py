@@ -49,6 +49,35 @@ def _scales(g, shape):
 
 
 # ---------------------------------------------------------------- routing
+def test_route_token_chunks(m):
+    """More tokens than one launch of the large-batch logits kernel takes (its
+    token rows stay below 2 GiB, 149,760 tokens at 7168): tokens on both sides of
+    the chunk boundary and in the ragged last tile match the oracle.  x comes
+    from torch's seeded generator on the device; the sampled rows go back to the
+    oracle."""
+    H, E, k = 7168, 16, 2
+    chunk = ((2 ** 31 - 1) // (H * 2)) // 64 * 64
+    T = chunk + 137
+    say(f"route token chunks T={T} H={H} E={E}")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn((T, H), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    g = np.random.default_rng(11)
+    w = _rand_bf16(g, (E, H), 0.02)
+    b = g.uniform(-0.1, 0.1, E).astype(np.float32)
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.moe_route_workspace_bytes(T, H, E), dtype=torch.uint8, device="cuda")
+    m.moe_route(x, bf16_dev(w), torch.from_numpy(b).cuda(), k, True, idx, wt, ws)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([np.arange(0, 64), np.arange(chunk - 70, chunk + 70), np.arange(T - 80, T),
+                                     g.integers(0, T, 64)]))
+    xs = np_bf16(x[torch.from_numpy(toks).cuda()])
+    del x
+    ridx, rw = oracle.route(xs, w, b, k, True)
+    np.testing.assert_array_equal(idx.cpu().numpy()[toks], ridx)
+    np.testing.assert_array_equal(wt.cpu().numpy()[toks], rw)
+
+
 @pytest.mark.parametrize("T,H,E,k,seed", [
     (1, 128, 16, 1, 0), (37, 256, 16, 2, 1), (64, 7168, 384, 8, 2), (300, 1024, 384, 8, 3),
     (130, 512, 1000, 16, 4), (64, 256, 8, 8, 5),
