@@ -193,6 +193,19 @@ __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         if (mb >= active_mb) continue;
+        // the block's addends are loaded before its first store (a store in
+        // between would make each later load wait for it: y may alias add); rows
+        // and columns past the matrix read a clamped in-bounds element, never used
+        uint32_t addv[4][CB];
+        if (!SPLIT && EPI == EPI_LINEAR && a.add) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int rl = min(16 * mb + 4 * j + ii, rows - 1);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    addv[ii][cb] = a.add[(size_t)(m0 + rl) * a.N0 + min(n0 + 16 * cb + r, a.N0 - 1)];
+            }
+        }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int rl = 16 * mb + 4 * j + ii;
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(256) void k_dense(DenseArgs a) {
                     const int col = n0 + 16 * cb + r;
                     if (col < a.N0) {
                         uint32_t yb = f32_to_bf16_bits(acc[mb][cb][ii]);
-                        if (a.add) yb = add_bits(yb, a.add[m * a.N0 + col]);
+                        if (a.add) yb = add_bits(yb, (uint16_t)addv[ii][cb]);
                         a.y[m * a.N0 + col] = (uint16_t)yb;
                     }
                 }
@@ -374,24 +387,49 @@ __global__ __launch_bounds__(256) void k_dense32(DenseArgs a) {
     for (int q = 0; q < R - 1; ++q)
         if (c + q < nch) step(c + q, sl[q]);
 
+    // Epilogue, in batches of MBB row blocks.  A batch's addend loads are all
+    // issued before its first store (a store in between would make each later
+    // load wait for it: y may alias add); rows and columns past the matrix read a
+    // clamped in-bounds element, never used.  192-row tiles take two batches,
+    // which keeps the addends out of scratch.
+    constexpr int MBB = M32 > 4 ? M32 / 2 : M32;
+    static_assert(M32 % MBB == 0, "epilogue batches");
 #pragma unroll
-    for (int mb = 0; mb < M32; ++mb) {
+    for (int mb0 = 0; mb0 < M32; mb0 += MBB) {
+        uint32_t addv[MBB][16][2];
+        if (EPI == EPI_LINEAR && a.add) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
-            if (rl >= rows) continue;
-            const size_t m = (size_t)(m0 + rl);
-            if (EPI == EPI_SWIGLU) {
-                const int col = n0 + c32;
-                if (col < a.N0) a.y[m * a.N0 + col] = (uint16_t)silu_mul_bits(acc[mb][0][i], acc[mb][1][i]);
-            } else {
+            for (int b = 0; b < MBB; ++b)
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    const int col = n0 + 32 * cb + c32;
-                    if (col < a.N0) {
-                        uint32_t yb = f32_to_bf16_bits(acc[mb][cb][i]);
-                        if (a.add) yb = add_bits(yb, a.add[m * a.N0 + col]);
-                        a.y[m * a.N0 + col] = (uint16_t)yb;
+                for (int i = 0; i < 16; ++i) {
+                    const int rl = min(32 * (mb0 + b) + 8 * (i >> 2) + 4 * kb + (i & 3), rows - 1);
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) {
+                        const int col = min(n0 + 32 * cb + c32, a.N0 - 1);
+                        addv[b][i][cb] = a.add[(size_t)(m0 + rl) * a.N0 + col];
+                    }
+                }
+        }
+#pragma unroll
+        for (int b = 0; b < MBB; ++b) {
+            const int mb = mb0 + b;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
+                if (rl >= rows) continue;
+                const size_t m = (size_t)(m0 + rl);
+                if (EPI == EPI_SWIGLU) {
+                    const int col = n0 + c32;
+                    if (col < a.N0) a.y[m * a.N0 + col] = (uint16_t)silu_mul_bits(acc[mb][0][i], acc[mb][1][i]);
+                } else {
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) {
+                        const int col = n0 + 32 * cb + c32;
+                        if (col < a.N0) {
+                            uint32_t yb = f32_to_bf16_bits(acc[mb][cb][i]);
+                            if (a.add) yb = add_bits(yb, (uint16_t)addv[b][i][cb]);
+                            a.y[m * a.N0 + col] = (uint16_t)yb;
+                        }
                     }
                 }
             }

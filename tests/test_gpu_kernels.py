@@ -577,6 +577,7 @@ def test_exact_linear_i8w_bitexact(m, M, N, K, seed):
     (16, 512, 2048, False, 11),     # split K, 16-row tiles
     (30, 320, 1024, True, 12),      # split K, 32-row tiles, ragged rows and columns
     (50, 128, 2560, True, 13),      # split K into splits of 2 and 3 chunks
+    (130, 320, 256, True, 14),      # 16x16 tiles unsplit with an addend: ragged rows and columns
 ])
 def test_linear_bf16(m, M, N, K, with_add, seed):
     say(f"linear M={M} N={N} K={K}")
