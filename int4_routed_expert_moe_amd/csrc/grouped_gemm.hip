@@ -467,22 +467,46 @@ __device__ __forceinline__ void grouped_tile(const GroupedArgs& a) {
         if constexpr (NACT == 0) {
             // bf16: all MB row blocks, each under a uniform branch on the tile's
             // active count (fewer registers than the instances: this kernel
-            // serves HBM-bound batches, where two waves per SIMD matter more)
+            // serves HBM-bound batches, where two waves per SIMD matter more).
+            // One stream of 4 MB (group, row block) products.  Fragment reads run
+            // two products ahead, unconditionally (inactive rows are staged too),
+            // so that no product waits on its own LDS read; the next group's
+            // weights are dequantised while the current group's products run.
             const int buf = c & 1;
+            constexpr int NS = 4 * MB;
+            constexpr int PFA = 2;
+            auto frag = [&](int st) __attribute__((always_inline)) {
+                return *reinterpret_cast<const half8_t*>(&As[buf][16 * (st % MB) + r][32 * (st / MB) + 8 * j]);
+            };
+            half8_t afr[NS];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                half8_t bf[CB];
-                dequant_step(sl, g, bf);
+            for (int q = 0; q < PFA; ++q) afr[q] = frag(q);
+            half8_t bfa[CB], bfb[CB];
+            dequant_step(sl, 0, bfa);
+            static_for<NS>([&](auto sc) __attribute__((always_inline)) {
+                constexpr int st = decltype(sc)::value;
+                constexpr int g = st / MB;
+                constexpr int mb = st % MB;
+                if constexpr (st + PFA < NS) afr[st + PFA] = frag(st + PFA);
+                half8_t(&cur)[CB] = (g & 1) ? bfb : bfa;
+                half8_t(&nxt)[CB] = (g & 1) ? bfa : bfb;
+                if (mb == 0 || mb < active_mb) {
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    if (mb < active_mb) {
-                        const half8_t af = *reinterpret_cast<const half8_t*>(&As[buf][16 * mb + r][32 * g + 8 * j]);
+                    for (int cb = 0; cb < CB; ++cb)
+                        acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[st], cur[cb], acc[mb][cb], 0, 0, 0);
+                }
+                // column blocks of group g+1 dequantised after product (g, mb)
+                if constexpr (g < 3) {
 #pragma unroll
-                        for (int cb = 0; cb < CB; ++cb)
-                            acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
+                    for (int cb = 0; cb < CB; ++cb) {
+                        if (cb * MB / CB == mb) {
+                            half2_t s2, c2;
+                            scale_pair(sl.S[cb][(g + 1) >> 1] >> (16 * ((g + 1) & 1)), s2, c2);
+                            nxt[cb] = dequant8(sl.B[cb][g + 1], s2, c2);
+                        }
                     }
                 }
-            }
+            });
         } else {
         constexpr int NS = 4 * NACT;
         constexpr int PF = EXACT ? 2 : 4;
