@@ -25,6 +25,9 @@ namespace {
 constexpr int kDKC = 128;
 constexpr int kDense32MinM = 256;   // rows from which the 32x32 tile kernel runs
 constexpr int kDense32TallM = 6144; // rows from which it takes 192-row tiles
+constexpr int kDense256MinTiles = 192;  // 256-row tiles from this many workgroups
+// 32-bit byte offsets within a 256-row tile; longer rows take the 16x16 kernel
+constexpr int kDense32MaxK = 1 << 22;
 constexpr int kDAStride = 136;  // bf16 per LDS row
 
 enum { EPI_LINEAR = 0, EPI_SWIGLU = 1 };
@@ -251,6 +254,62 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Epilogue of the 32x32 dense kernels: element i of lane (c32, kb) in row
+// block mb is tile row 32 mb + 8(i/4) + 4 kb + i%4, column n0 + 32 cb + c32
+// (linear) or n0 + c32 (swiglu: block 0 gate, block 1 up).
+template <int M32, int EPI>
+__device__ __forceinline__ void dense32_epilogue(const DenseArgs& a, const f32x16_t (&acc)[M32][2], int m0,
+                                                 int rows, int n0, int c32, int kb) {
+    // In batches of MBB row blocks.  A batch's addend loads are all
+    // issued before its first store (a store in between would make each later
+    // load wait for it: y may alias add); rows and columns past the matrix read a
+    // clamped in-bounds element, never used.  Tiles of more than 128 rows take
+    // two batches, which keeps the addends out of scratch.
+    constexpr int MBB = M32 > 4 ? M32 / 2 : M32;
+    static_assert(M32 % MBB == 0, "epilogue batches");
+#pragma unroll
+    for (int mb0 = 0; mb0 < M32; mb0 += MBB) {
+        uint32_t addv[MBB][16][2];
+        if (EPI == EPI_LINEAR && a.add) {
+#pragma unroll
+            for (int b = 0; b < MBB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rl = min(32 * (mb0 + b) + 8 * (i >> 2) + 4 * kb + (i & 3), rows - 1);
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) {
+                        const int col = min(n0 + 32 * cb + c32, a.N0 - 1);
+                        addv[b][i][cb] = a.add[(size_t)(m0 + rl) * a.N0 + col];
+                    }
+                }
+        }
+#pragma unroll
+        for (int b = 0; b < MBB; ++b) {
+            const int mb = mb0 + b;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
+                if (rl >= rows) continue;
+                const size_t m = (size_t)(m0 + rl);
+                if (EPI == EPI_SWIGLU) {
+                    const int col = n0 + c32;
+                    if (col < a.N0) a.y[m * a.N0 + col] = (uint16_t)silu_mul_bits(acc[mb][0][i], acc[mb][1][i]);
+                } else {
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb) {
+                        const int col = n0 + 32 * cb + c32;
+                        if (col < a.N0) {
+                            uint32_t yb = f32_to_bf16_bits(acc[mb][cb][i]);
+                            if (a.add) yb = add_bits(yb, (uint16_t)addv[b][i][cb]);
+                            a.y[m * a.N0 + col] = (uint16_t)yb;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Row tiles of 32*M32 rows on v_mfma_f32_32x32x16_bf16 (one wave per SIMD
 // drives that shape near its peak; the 16x16x32 shape above stops near 1.4 PF
 // at this occupancy).  A workgroup is 4 waves; each wave owns two 32-column
@@ -299,13 +358,14 @@ __global__ __launch_bounds__(256) void k_dense32(DenseArgs a) {
     // 16 contiguous bytes); wave w moves rows 4*A_ITERS*w + 4*it + lane/16 (rows
     // past the tile read the tile's first row; their products are never stored)
     auto srow_of = [&](int it) { return 4 * A_ITERS * wave + 4 * it + (lane >> 4); };
-    uint32_t aoff[A_ITERS];
+    const uint16_t* xt = a.x + (size_t)m0 * K;  // the tile's first row
+    uint32_t aoff[A_ITERS];                       // element offsets within the tile
 #pragma unroll
     for (int it = 0; it < A_ITERS; ++it)
-        aoff[it] = (uint32_t)((m0 + (srow_of(it) < rows ? srow_of(it) : 0)) * K + (lane & 15) * 8);
+        aoff[it] = (uint32_t)(srow_of(it) < rows ? srow_of(it) : 0) * (uint32_t)K + (uint32_t)(lane & 15) * 8u;
     u32x4_t Aq[A_ITERS];
     auto load_piece = [&](int it, int c) __attribute__((always_inline)) {
-        Aq[it] = *reinterpret_cast<const u32x4_t*>(a.x + aoff[it] + (size_t)c * kDKC);
+        Aq[it] = *reinterpret_cast<const u32x4_t*>(xt + aoff[it] + (size_t)c * kDKC);
     };
     auto store_piece = [&](int it, int buf) __attribute__((always_inline)) {
         *reinterpret_cast<u32x4_t*>(&As[buf][srow_of(it)][(lane & 15) * 8]) = Aq[it];
@@ -387,54 +447,163 @@ __global__ __launch_bounds__(256) void k_dense32(DenseArgs a) {
     for (int q = 0; q < R - 1; ++q)
         if (c + q < nch) step(c + q, sl[q]);
 
-    // Epilogue, in batches of MBB row blocks.  A batch's addend loads are all
-    // issued before its first store (a store in between would make each later
-    // load wait for it: y may alias add); rows and columns past the matrix read a
-    // clamped in-bounds element, never used.  192-row tiles take two batches,
-    // which keeps the addends out of scratch.
-    constexpr int MBB = M32 > 4 ? M32 / 2 : M32;
-    static_assert(M32 % MBB == 0, "epilogue batches");
+    dense32_epilogue<M32, EPI>(a, acc, m0, rows, n0, c32, kb);
+}
+
+// The 32x32 dense kernel for 256-row tiles (M32 = 8).  The same products and
+// order as k_dense32, but the A tile is staged by buffer-to-LDS loads, so that
+// no registers hold it in flight: two LDS buffers of 256 unpadded 256-byte rows
+// whose 16-byte units are XOR-swizzled by the row (unit u of row r at u ^ (r mod
+// 16)), so that the fragment reads stay free of bank conflicts.  Chunk c+1 is
+// loaded into the other buffer while chunk c is multiplied (its last readers
+// finished before the previous barrier).  Taller tiles read each weight line
+// for twice the rows of the 128-row ones.
+template <int M32, int EPI, int R>
+__global__ __launch_bounds__(256) void k_dense32_dma(DenseArgs a) {
+    constexpr int BM = 32 * M32;
+    constexpr int A_ITERS = BM / 16;  // staging instructions per wave per chunk (4 rows each)
+    constexpr int NS = 8 * M32;       // (K step, row block) products per chunk
+    static_assert(A_ITERS * 4 * 4 == BM && 2 * A_ITERS <= NS, "staging: 4 rows per wave instruction");
+    // two separate LDS objects, so that the compiler can tell a fragment read of
+    // one buffer from the loads into the other
+    __shared__ __attribute__((aligned(16))) uint16_t As0[BM][kDKC];
+    __shared__ __attribute__((aligned(16))) uint16_t As1[BM][kDKC];
+    auto tile = [&](auto bc) -> uint16_t(&)[BM][kDKC] {
+        if constexpr (decltype(bc)::value == 0) return As0;
+        else return As1;
+    };
+
+    const long L = xcd_logical_block(a.per_xcd);
+    if (L >= a.n_logical) return;
+    const int nc = (int)(L % a.n_chunks);
+    const int tm = (int)(L / a.n_chunks);
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c32 = lane & 31;
+    const int kb = lane >> 5;
+    const int K = a.K;
+    const int m0 = tm * BM;
+    const int rows = min(BM, a.M - m0);
+    const int nch = K / kDKC;
+
+    // weight rows past N read the last row (never stored)
+    const int n0 = EPI == EPI_SWIGLU ? nc * 128 + wave * 32 : nc * 256 + wave * 64;
+    const uint16_t* wrow[2];
 #pragma unroll
-    for (int mb0 = 0; mb0 < M32; mb0 += MBB) {
-        uint32_t addv[MBB][16][2];
-        if (EPI == EPI_LINEAR && a.add) {
-#pragma unroll
-            for (int b = 0; b < MBB; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int rl = min(32 * (mb0 + b) + 8 * (i >> 2) + 4 * kb + (i & 3), rows - 1);
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) {
-                        const int col = min(n0 + 32 * cb + c32, a.N0 - 1);
-                        addv[b][i][cb] = a.add[(size_t)(m0 + rl) * a.N0 + col];
-                    }
-                }
-        }
-#pragma unroll
-        for (int b = 0; b < MBB; ++b) {
-            const int mb = mb0 + b;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int rl = 32 * mb + 8 * (i >> 2) + 4 * kb + (i & 3);
-                if (rl >= rows) continue;
-                const size_t m = (size_t)(m0 + rl);
-                if (EPI == EPI_SWIGLU) {
-                    const int col = n0 + c32;
-                    if (col < a.N0) a.y[m * a.N0 + col] = (uint16_t)silu_mul_bits(acc[mb][0][i], acc[mb][1][i]);
-                } else {
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb) {
-                        const int col = n0 + 32 * cb + c32;
-                        if (col < a.N0) {
-                            uint32_t yb = f32_to_bf16_bits(acc[mb][cb][i]);
-                            if (a.add) yb = add_bits(yb, (uint16_t)addv[b][i][cb]);
-                            a.y[m * a.N0 + col] = (uint16_t)yb;
-                        }
-                    }
-                }
-            }
-        }
+    for (int cb = 0; cb < 2; ++cb) {
+        const int n = min(EPI == EPI_SWIGLU ? n0 + c32 : n0 + 32 * cb + c32, a.N0 - 1);
+        wrow[cb] = (EPI == EPI_SWIGLU && cb == 1 ? a.w1 : a.w0) + (size_t)n * K + 64 * kb;
     }
+
+    // staging instruction it of this wave writes tile rows 4 A_ITERS wave + 4 it
+    // .. +3 (lane l: row + l/16, physical unit l mod 16, which holds logical unit
+    // (l mod 16) ^ (row mod 16)), read through a descriptor over the tile's rows;
+    // rows past the matrix read the tile's first row (their products are never
+    // stored)
+    const __amdgpu_buffer_rsrc_t ra =
+        buffer_rsrc(a.x + (size_t)m0 * K, (uint32_t)rows * (uint32_t)K * 2u);
+    uint32_t aoff[A_ITERS];
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) {
+        const int row = 4 * A_ITERS * wave + 4 * it + (lane >> 4);
+        const uint32_t unit = (uint32_t)((lane & 15) ^ (row & 15));
+        aoff[it] = ((uint32_t)(row < rows ? row : 0) * (uint32_t)K + unit * 8u) * 2u;
+    }
+    auto dma_piece = [&](int it, int c, auto bc) __attribute__((always_inline)) {
+        buffer_load_lds16(ra, &tile(bc)[4 * A_ITERS * wave + 4 * it][0], aoff[it], (uint32_t)c * (kDKC * 2));
+    };
+
+    struct Slot {
+        u32x4_t B[2][8];  // per column block and step: 8 bf16 of the lane's weight row
+    };
+    auto load_B = [&](int c, Slot& sl) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                sl.B[cb][q] = *reinterpret_cast<const u32x4_t*>(wrow[cb] + (size_t)c * kDKC + 8 * q);
+    };
+
+    f32x16_t acc[M32][2];
+#pragma unroll
+    for (int mb = 0; mb < M32; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][cb][i] = 0.0f;
+
+    // products of chunk c from buffer BUF; the staging loads of chunk c+1 into
+    // the other buffer spread over the first half
+    auto compute = [&](auto bc, int c, const Slot& sl) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bc)::value;
+        constexpr int PF = 4;
+        const int swz = c32 & 15;
+        auto frag = [&](int p) __attribute__((always_inline)) {
+            const int unit = (8 * kb + p / M32) ^ swz;
+            return __builtin_bit_cast(bf16x8_t,
+                                      *reinterpret_cast<const u32x4_t*>(&tile(bc)[32 * (p % M32) + c32][8 * unit]));
+        };
+        bf16x8_t afr[NS];
+#pragma unroll
+        for (int q = 0; q < PF; ++q) afr[q] = frag(q);
+        const int cs = min(c + 1, nch - 1);
+        static_for<NS>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int p = decltype(pc)::value;
+            constexpr int st = p / M32;
+            constexpr int mb = p % M32;
+            if constexpr (p + PF < NS) afr[p + PF] = frag(p + PF);
+            static_for<A_ITERS>([&](auto ic) __attribute__((always_inline)) {
+                constexpr int i = decltype(ic)::value;
+                if constexpr (i * NS / (2 * A_ITERS) == p)
+                    dma_piece(i, cs, std::integral_constant<int, 1 - BUF>{});
+            });
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    afr[p], __builtin_bit_cast(bf16x8_t, sl.B[cb][st]), acc[mb][cb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0x0002);
+        });
+    };
+
+    // Loads issued, in order: weights of chunks 0 .. R-2, staging 0, weights R-1 |
+    // step c: staging c+1 (first half of the products), weights c+R (16 per lane)
+    // | staging c+1 has landed once at most 16 younger loads are outstanding (the
+    // weights of c+R), and in the prologue staging 0 too (weights R-1).  Chunk
+    // indices past the end are clamped: redundant in-bounds loads, never read.
+    static_assert(R == 2 || R == 3, "ring depth");
+    Slot sl[R];
+#pragma unroll
+    for (int q = 0; q < R - 1; ++q) load_B(min(q, nch - 1), sl[q]);
+#pragma unroll
+    for (int it = 0; it < A_ITERS; ++it) dma_piece(it, 0, std::integral_constant<int, 0>{});
+    load_B(min(R - 1, nch - 1), sl[R - 1]);
+    wait_vmcnt<16>();
+    lds_barrier();
+    auto step = [&](auto bc, int c, Slot& cur) __attribute__((always_inline)) {
+        compute(bc, c, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        load_B(min(c + R, nch - 1), cur);
+        wait_vmcnt<16>();
+        lds_barrier();
+    };
+    // unrolled by lcm(2, R): buffers and slots stay compile-time choices
+    constexpr int U = R == 2 ? 2 : 6;
+    int c = 0;
+    for (; c + U <= nch; c += U) {
+        static_for<U>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            step(std::integral_constant<int, q % 2>{}, c + q, sl[q % R]);
+        });
+    }
+    static_for<U - 1>([&](auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        if (c + q < nch) step(std::integral_constant<int, q % 2>{}, c + q, sl[q % R]);
+    });
+    wait_vmcnt<0>();  // the trailing (redundant) staging loads land before the wave ends
+
+    dense32_epilogue<M32, EPI>(a, acc, m0, rows, n0, c32, kb);
 }
 
 // Sum the split-K partials in ascending split order, then the epilogue.
@@ -542,15 +711,27 @@ int run_dense(int epi, const uint16_t* x, const uint16_t* w0, const uint16_t* w1
         else hipLaunchKernelGGL(k_dense_reduce<EPI_LINEAR>, g, dim3(256), 0, st, a.part, p.ksplit, M, N0, Ntot, add, y);
         return moe::launch_status(what);
     }
-    if (M >= kDense32MinM) {
+    if (M >= kDense32MinM && K <= kDense32MaxK) {
+        const int cols = sw ? 128 : 256;
+        const int n_chunks = (N0 + cols - 1) / cols;
+        if ((long)((M + 255) / 256) * n_chunks >= kDense256MinTiles) {
+            // 256-row tiles wherever they still give most CUs a workgroup
+            a.n_chunks = n_chunks;
+            a.tiles_m = (M + 255) / 256;
+            a.n_logical = (long)a.tiles_m * a.n_chunks;
+            a.per_xcd = moe::per_xcd(a.n_logical);
+            const dim3 grid(8 * a.per_xcd), block(256);
+            if (sw) hipLaunchKernelGGL((k_dense32_dma<8, EPI_SWIGLU, 2>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_dense32_dma<8, EPI_LINEAR, 2>), grid, block, 0, st, a);
+            return moe::launch_status(what);
+        }
         // 32x32 tiles of 128 rows, or 192 from kDense32TallM rows (the weights,
         // read from L2 once per row tile, dominate a tile's operand traffic:
         // taller tiles re-read them less often).  The 128-row tiles keep a
         // 3-slot weight ring; the 192-row tiles' accumulators leave room for 2
         // slots only (3 spill).  Measured on 2048 rows, 192-row tiles left too
         // few workgroups (0.18 -> 0.22 ms); on 8192 rows they gained 10%.
-        const int cols = sw ? 128 : 256;
-        a.n_chunks = (N0 + cols - 1) / cols;
+        a.n_chunks = n_chunks;
         const int m32 = M >= kDense32TallM ? 6 : 4;
         a.tiles_m = (M + 32 * m32 - 1) / (32 * m32);
         a.n_logical = (long)a.tiles_m * a.n_chunks;

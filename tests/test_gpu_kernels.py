@@ -578,6 +578,8 @@ def test_exact_linear_i8w_bitexact(m, M, N, K, seed):
     (30, 320, 1024, True, 12),      # split K, 32-row tiles, ragged rows and columns
     (50, 128, 2560, True, 13),      # split K into splits of 2 and 3 chunks
     (130, 320, 256, True, 14),      # 16x16 tiles unsplit with an addend: ragged rows and columns
+    (2000, 6464, 384, True, 15),    # 256-row tiles: ragged rows, a part-filled column chunk, odd chunk count
+    (1800, 7168, 256, False, 16),   # 256-row tiles, no addend
 ])
 def test_linear_bf16(m, M, N, K, with_add, seed):
     say(f"linear M={M} N={N} K={K}")
@@ -597,7 +599,8 @@ def test_linear_bf16(m, M, N, K, with_add, seed):
 @pytest.mark.parametrize("M,H,I,seed", [(64, 256, 128, 0), (64, 7168, 2048, 1), (130, 512, 192, 2),
                                         (300, 256, 192, 3),     # 32x32 tiles, ragged rows and columns
                                         (4096, 128, 2048, 4),   # 32x32 tiles, many row tiles
-                                        (6150, 256, 192, 5)])   # 192-row tiles, ragged rows and columns
+                                        (6150, 256, 192, 5),    # 192-row tiles, ragged rows and columns
+                                        (2000, 384, 3264, 6)])  # 256-row tiles, ragged rows and columns
 def test_dense_swiglu_and_silu_mul(m, M, H, I, seed):
     say(f"dense swiglu M={M} H={H} I={I}")
     g = np.random.default_rng(seed)
