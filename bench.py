@@ -53,6 +53,9 @@ def parse():
                          "report it under 'prefill' (default: on for the default decode workload)")
     ap.add_argument("--no-prefill-leg", dest="prefill_leg", action="store_false")
     ap.add_argument("--no-hbm-probe", action="store_true", help="skip the streaming read and copy probes")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the forward recorded as a HIP graph (MoELayer.capture) instead of "
+                         "eager forwards; the per-call times still come from eager forwards")
     ap.add_argument("--gemm-reference", action="store_true",
                     help="also time torch's dense bf16 GEMM (hipBLASLt) at the prefill gate/up and down shapes, "
                          "a practical matrix-core reference under this part's clock behaviour")
@@ -209,20 +212,25 @@ def roofline(cfg, counts, kernel_ms):
     return roof, layer_bytes, layer_flops, active
 
 
-def time_layer(layer, x, steps, warmup, kernel_steps):
+def time_layer(layer, x, steps, warmup, kernel_steps, graph=False):
     """ms per step over exactly `steps` timed forwards (after `warmup`), between two
     synchronisations, and the per-call event durations of `kernel_steps` more forwards
-    (every call on the launch stream)."""
+    (every call on the launch stream).  graph: the timed forwards are replays of the
+    forward recorded as a HIP graph on x."""
     import torch
+    run = layer.forward
+    if graph:
+        g = layer.capture(x)
+        run = lambda _x: g.replay()  # noqa: E731  (x is the graph's input buffer)
     for _ in range(warmup):
-        layer.forward(x)
+        run(x)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(steps):
-        layer.forward(x)
+        run(x)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -498,7 +506,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    ms_per_step, kernel_ms, wall = time_layer(layer, x, args.steps, args.warmup, args.kernel_steps)
+    ms_per_step, kernel_ms, wall = time_layer(layer, x, args.steps, args.warmup, args.kernel_steps, args.graph)
     counts = layer.workspace(T)["counts"].cpu().numpy()
     roof, layer_bytes, layer_flops, active = roofline(cfg, counts, kernel_ms)
 
@@ -535,7 +543,7 @@ def main():
         "wall_s_timed": wall,
         "setup_s": t_gen,
         "run": {"warmup": args.warmup, "steps": args.steps, "kernel_steps": args.kernel_steps,
-                "side_stream_min_t": MoELayer.SIDE_STREAM_MIN_T},
+                "side_stream_min_t": MoELayer.SIDE_STREAM_MIN_T, "graph": args.graph},
     }
     if cfg["mode"] == "exact":
         line["layer_roofline"]["int8_frac"] = layer_flops / step_s / (INT8_PEAK_TOPS * 1e12)
@@ -547,7 +555,8 @@ def main():
         if cfg3["layer_seed"] != cfg["layer_seed"] or cfg3["H"] != cfg["H"]:
             sys.exit("--prefill-leg needs a workload that shares the prefill workload's layer")
         x3 = torch.from_numpy(synthetic.gen_x(cfg3).view(np.int16)).cuda().view(torch.bfloat16)
-        ms3, kms3, wall3 = time_layer(layer, x3, args.steps, args.warmup, max(3, args.kernel_steps // 2))
+        ms3, kms3, wall3 = time_layer(layer, x3, args.steps, args.warmup, max(3, args.kernel_steps // 2),
+                                      args.graph)
         counts3 = layer.workspace(cfg3["T"])["counts"].cpu().numpy()
         roof3, lb3, lf3, active3 = roofline(cfg3, counts3, kms3)
         line["prefill"] = {

@@ -258,6 +258,10 @@ class MoELayer:
             mark("latent_up")
         return w["out"]
 
+    def capture(self, x: torch.Tensor) -> "LayerGraph":
+        """Record one forward on the buffer ``x`` as a HIP graph (see LayerGraph)."""
+        return LayerGraph(self, x)
+
     def _shared_expert(self, x, w, mark=None):
         _m.moe_dense_swiglu_bf16(x, self.shared["wg"], self.shared["wu"], w["shared_h"], w["shared_ws"])
         if mark:
@@ -267,3 +271,35 @@ class MoELayer:
             mark("shared_down")
 
     __call__ = forward
+
+
+class LayerGraph:
+    """One forward of a layer for a fixed batch size, recorded as a HIP graph
+    (torch.cuda.CUDAGraph): a replay relaunches every call of the forward -- the
+    same kernels, grids and buffers, the shared expert's side stream included --
+    with one host call, so a decode loop pays no per-call launch gaps.
+
+    ``x`` is the graph's input buffer: write the next batch into it (same shape),
+    then ``replay()``.  The output buffer that replay() returns is the layer's
+    workspace output for that T, overwritten by every replay and by eager
+    forwards of the same T.  The forward allocates nothing and issues no memory
+    set or copy, so the graph holds kernel nodes and the stream-fork/join
+    dependencies only."""
+
+    def __init__(self, layer: MoELayer, x: torch.Tensor):
+        self.layer = layer
+        self.x = x
+        # one eager forward first, off the capture: it allocates the workspace
+        # for this T, the side stream and its events
+        s = torch.cuda.Stream(device=x.device)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            layer.forward(x)
+        torch.cuda.current_stream().wait_stream(s)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.out = layer.forward(x)
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        return self.out
