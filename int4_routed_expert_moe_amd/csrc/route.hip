@@ -19,6 +19,8 @@ namespace {
 constexpr int kRouteTok = 64;   // tokens per block
 constexpr int kRouteKC = 64;    // hidden elements per block sum (one LDS chunk)
 constexpr int kRouterWaves = 4; // waves (16 experts each) per many-token logits workgroup
+// grids of up to this many workgroups (one per CU) take the two-chain logits kernel
+constexpr long kRouterPairMaxTiles = 256;
 
 // Stage 64 rows x 64 hidden elements of a bf16 matrix as fp32, transposed to
 // [i][row]; rows at or past `limit` are zero.  Two 16-byte pieces per thread.
@@ -181,6 +183,149 @@ __global__ __launch_bounds__(64 * NW) void k_router_mfma(const uint16_t* __restr
     if (b < NB) step(B0, b);
     if (b + 1 < NB) step(B1, b + 1);
     wait_vmcnt<0>();  // the trailing redundant loads land before the workgroup ends
+
+    const int ex = e0 + 16 * wave + (lane & 15);
+    if (ex >= E) return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int tok = t0 + 16 * (i >> 2) + 4 * (lane >> 4) + (i & 3);
+        if (tok < T) logits[(size_t)tok * E + ex] = tot[i];
+    }
+}
+
+// k_router_mfma for grids of at most one workgroup per CU (2048 tokens at 384
+// experts: 192 workgroups): each wave then runs alone on its SIMD, and its one
+// chain of dependent matrix-core steps leaves the pipe idle between steps.
+// Here a wave multiplies two consecutive hidden blocks at once, as two
+// independent chains whose steps alternate; the two block sums still enter the
+// total in block order, so the results are those of k_router_mfma.  Tiles go
+// through four LDS buffers in two pairs (64 KB, two workgroups per CU at most,
+// which is why larger grids keep the three-buffer kernel).
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_router_mfma_pair(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ w, int T, int H, int E,
+                                                              float* __restrict__ logits, int n_et,
+                                                              int per_xcd) {
+    constexpr int RW = 16 * NW;           // router rows per tile
+    constexpr int NI = 8 + RW / 8;        // 1-KB load instructions per block (token tile: 8)
+    static_assert(NI % NW == 0, "load instructions shared evenly by the waves");
+    constexpr int PER = NI / NW;          // this wave's load instructions per block
+    // four tile buffers in two pairs: a step multiplies the two blocks of one pair
+    // while the next two blocks load into the other (separate LDS objects, so that
+    // the compiler can tell a read of one buffer from the loads into another)
+    __shared__ __attribute__((aligned(16))) uint16_t X0[8][64][8], X1[8][64][8], X2[8][64][8], X3[8][64][8];
+    __shared__ __attribute__((aligned(16))) uint16_t W0[8][RW][8], W1[8][RW][8], W2[8][RW][8], W3[8][RW][8];
+    auto xt = [&](auto bc) -> uint16_t(&)[8][64][8] {
+        if constexpr (decltype(bc)::value == 0) return X0;
+        else if constexpr (decltype(bc)::value == 1) return X1;
+        else if constexpr (decltype(bc)::value == 2) return X2;
+        else return X3;
+    };
+    auto wt = [&](auto bc) -> uint16_t(&)[8][RW][8] {
+        if constexpr (decltype(bc)::value == 0) return W0;
+        else if constexpr (decltype(bc)::value == 1) return W1;
+        else if constexpr (decltype(bc)::value == 2) return W2;
+        else return W3;
+    };
+
+    const long L = xcd_logical_block(per_xcd);
+    const long n_tt = (T + kRouteTok - 1) / kRouteTok;
+    if (L >= n_tt * n_et) return;
+    const int t0 = (int)(L / n_et) * kRouteTok;
+    const int e0 = (int)(L % n_et) * RW;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int NB = H / kRouteKC;
+
+    // this wave's load instructions j = wave + NW m: j < 8 is piece j of the
+    // token tile (lane l: row l); j >= 8 covers router slots 64 (j - 8) + l of
+    // the [piece][row] layout
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, (uint32_t)((size_t)T * H * 2));
+    const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(w, (uint32_t)((size_t)E * H * 2));
+    uint32_t voff[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+        const int j = wave + NW * m;
+        if (j < 8) {
+            voff[m] = ((uint32_t)min(t0 + lane, T - 1) * (uint32_t)H + 8u * (uint32_t)j) * 2u;
+        } else {
+            const int s = 64 * (j - 8) + lane;
+            voff[m] = ((uint32_t)min(e0 + s % RW, E - 1) * (uint32_t)H + 8u * (uint32_t)(s / RW)) * 2u;
+        }
+    }
+    auto load_block = [&](int b, auto bc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int j = wave + NW * m;
+            if (j < 8) buffer_load_lds16(xr, &xt(bc)[j][0][0], voff[m], (uint32_t)b * (kRouteKC * 2));
+            else buffer_load_lds16(wr, &wt(bc)[0][0][0] + 64 * 8 * (j - 8), voff[m], (uint32_t)b * (kRouteKC * 2));
+        }
+    };
+    auto elem = [](const u32x4_t& v, int q) __attribute__((always_inline)) {
+        return __uint_as_float((q & 1) ? (v[q >> 1] & 0xFFFF0000u) : (v[q >> 1] << 16));
+    };
+    f32x16_t tot = {};
+    // two consecutive blocks as two independent 64-step chains from zero, their
+    // steps interleaved (one chain's latency hides behind the other's), then the
+    // two block sums into the total in block order
+    auto block2 = [&](auto bc0, auto bc1) __attribute__((always_inline)) {
+        f32x16_t p0 = {}, p1 = {};
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const u32x4_t xa0 = *reinterpret_cast<const u32x4_t*>(&xt(bc0)[g][lane][0]);
+            const u32x4_t wa0 = *reinterpret_cast<const u32x4_t*>(&wt(bc0)[g][16 * wave + (lane & 15)][0]);
+            const u32x4_t xa1 = *reinterpret_cast<const u32x4_t*>(&xt(bc1)[g][lane][0]);
+            const u32x4_t wa1 = *reinterpret_cast<const u32x4_t*>(&wt(bc1)[g][16 * wave + (lane & 15)][0]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                p0 = __builtin_amdgcn_mfma_f32_16x16x1f32(elem(xa0, q), elem(wa0, q), p0, 0, 0, 0);
+                p1 = __builtin_amdgcn_mfma_f32_16x16x1f32(elem(xa1, q), elem(wa1, q), p1, 0, 0, 0);
+            }
+        }
+        tot = tot + p0;
+        tot = tot + p1;
+    };
+    // one block: 64 dependent steps from zero, then the block sum into the total
+    auto block1 = [&](auto bc) __attribute__((always_inline)) {
+        f32x16_t part = {};
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const u32x4_t xa = *reinterpret_cast<const u32x4_t*>(&xt(bc)[g][lane][0]);
+            const u32x4_t wa = *reinterpret_cast<const u32x4_t*>(&wt(bc)[g][16 * wave + (lane & 15)][0]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                part = __builtin_amdgcn_mfma_f32_16x16x1f32(elem(xa, q), elem(wa, q), part, 0, 0, 0);
+        }
+        tot = tot + part;
+    };
+    // step over blocks b, b+1 in pair P (buffers 2P, 2P+1): blocks b+2, b+3 load
+    // into the other pair (read last in the previous step, before its barrier)
+    auto step2 = [&](auto pc, int b) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        load_block(min(b + 2, NB - 1), std::integral_constant<int, 2 * (1 - P)>{});
+        load_block(min(b + 3, NB - 1), std::integral_constant<int, 2 * (1 - P) + 1>{});
+        block2(std::integral_constant<int, 2 * P>{}, std::integral_constant<int, 2 * P + 1>{});
+        wait_vmcnt<0>();  // this wave's loads of blocks b+2, b+3 have landed
+        lds_barrier();
+    };
+    constexpr std::integral_constant<int, 0> P0{};
+    constexpr std::integral_constant<int, 1> P1{};
+    load_block(0, std::integral_constant<int, 0>{});
+    load_block(min(1, NB - 1), std::integral_constant<int, 1>{});
+    wait_vmcnt<0>();
+    lds_barrier();
+    int b = 0;
+    for (; b + 4 <= NB; b += 4) {
+        step2(P0, b);
+        step2(P1, b + 2);
+    }
+    // 0..3 blocks left, the next two (if any) in buffers 0 and 1
+    if (NB - b >= 2) {
+        step2(P0, b);
+        if (NB - b == 3) block1(std::integral_constant<int, 2>{});
+    } else if (NB - b == 1) {
+        block1(std::integral_constant<int, 0>{});
+    }
 
     const int ex = e0 + 16 * wave + (lane & 15);
     if (ex >= E) return;
@@ -436,9 +581,14 @@ int route_impl(const uint16_t* x, const uint16_t* w_router, const float* bias, i
         const int n_et = (E + 16 * NW - 1) / (16 * NW);
         for (long c0 = 0; c0 < T; c0 += tc) {
             const int Tc = (int)std::min<long>(tc, (long)T - c0);
-            const int per_xcd = moe::per_xcd((long)n_et * ((Tc + kRouteTok - 1) / kRouteTok));
-            hipLaunchKernelGGL(k_router_mfma<NW>, dim3(8 * per_xcd), dim3(64 * NW), 0, st, x + (size_t)c0 * H,
-                               w_router, Tc, H, E, logits + (size_t)c0 * E, n_et, per_xcd);
+            const long tiles = (long)n_et * ((Tc + kRouteTok - 1) / kRouteTok);
+            const int per_xcd = moe::per_xcd(tiles);
+            if (tiles <= kRouterPairMaxTiles)
+                hipLaunchKernelGGL(k_router_mfma_pair<NW>, dim3(8 * per_xcd), dim3(64 * NW), 0, st,
+                                   x + (size_t)c0 * H, w_router, Tc, H, E, logits + (size_t)c0 * E, n_et, per_xcd);
+            else
+                hipLaunchKernelGGL(k_router_mfma<NW>, dim3(8 * per_xcd), dim3(64 * NW), 0, st, x + (size_t)c0 * H,
+                                   w_router, Tc, H, E, logits + (size_t)c0 * E, n_et, per_xcd);
         }
     }
     int rc = launch_status("moe_route logits");

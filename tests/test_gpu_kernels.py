@@ -81,11 +81,16 @@ def test_route_token_chunks(m):
 @pytest.mark.parametrize("T,H,E,k,seed", [
     (1, 128, 16, 1, 0), (37, 256, 16, 2, 1), (64, 7168, 384, 8, 2), (300, 1024, 384, 8, 3),
     (130, 512, 1000, 16, 4), (64, 256, 8, 8, 5),
-    (300, 512, 100, 4, 6),      # large-batch path, ragged last expert tile
-    (8192, 128, 384, 8, 7),     # large-batch path, two hidden blocks
-    (300, 64, 50, 4, 8),        # large-batch path, one hidden block, ragged tokens and experts
-    (260, 320, 70, 6, 9),       # large-batch path, five hidden blocks (loop plus both tail steps)
-    (2048, 7168, 384, 8, 10),   # large-batch path at the full hidden size
+    # large-batch paths: up to 256 workgroups (64 tokens x 64 experts each) the
+    # two-chain kernel (blocks in pairs), above it the one-chain kernel
+    (300, 512, 100, 4, 6),      # two-chain, ragged last expert tile
+    (8192, 128, 384, 8, 7),     # one-chain, two hidden blocks
+    (300, 64, 50, 4, 8),        # two-chain, one hidden block, ragged tokens and experts
+    (260, 320, 70, 6, 9),       # two-chain, five hidden blocks (a loop pass plus a single block)
+    (400, 192, 64, 4, 12),      # two-chain, three hidden blocks (a pair plus a single block)
+    (300, 448, 64, 4, 13),      # two-chain, seven hidden blocks (a loop pass, a pair and a single block)
+    (17000, 320, 70, 6, 11),    # one-chain, five hidden blocks (loop plus both tail steps), ragged
+    (2048, 7168, 384, 8, 10),   # two-chain at the full hidden size (192 workgroups)
 ])
 def test_route_bitexact(m, T, H, E, k, seed):
     say(f"route T={T} H={H} E={E} k={k}")
