@@ -460,7 +460,7 @@ def counters_summary(args, cfg):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     from int4_routed_expert_moe_amd import synthetic

@@ -200,7 +200,7 @@ int moe_int4_prepack(const uint8_t* packed, const uint16_t* scale, int E, int N,
  * (device int32, 4-byte aligned, overwritten) and returns MOE_ERR_UNSUPPORTED
  * with the count in the error detail when there is any, else MOE_OK.  scale
  * is n bf16 values (2-byte aligned), in either layout.  Unlike every other
- * call it synchronises `stream` to return its verdict: a weight-load step,
+ * call it synchronises `stream` to return its result: a weight-load step,
  * not for the forward path.  n == 0 returns MOE_OK. */
 int moe_int4_check_scales(const uint16_t* scale, size_t n, int32_t* count, void* stream);
 
