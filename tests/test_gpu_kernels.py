@@ -345,6 +345,8 @@ def _routing(g, T, E, k, skew=False):
     (700, 1024, 512, 6, 2, False, 7),    # gate/up 8 K chunks, 2 per item; down 4 K chunks, 4 per item
     (500, 1536, 384, 5, 2, True, 8),     # gate/up 1 per item; down 3 K chunks (the least), 2 per item
     (700, 1280, 512, 6, 2, False, 9),    # gate/up 10 K chunks, 2 per item; down 1 per item
+    (200, 512, 256, 8, 2, False, 10),    # mid-size segments (about 50 rows): tiles of 3 row blocks, split segments
+    (150, 768, 384, 6, 2, True, 11),     # the same, skewed (one long segment, empty experts)
 ])
 def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     say(f"grouped bf16 T={T} H={H} I={I} E={E} k={k}")
