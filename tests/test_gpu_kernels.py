@@ -347,6 +347,7 @@ def _routing(g, T, E, k, skew=False):
     (700, 1280, 512, 6, 2, False, 9),    # gate/up 10 K chunks, 2 per item; down 1 per item
     (200, 512, 256, 8, 2, False, 10),    # mid-size segments (about 50 rows): tiles of 3 row blocks, split segments
     (150, 768, 384, 6, 2, True, 11),     # the same, skewed (one long segment, empty experts)
+    (100, 256, 128, 32, 12, False, 12),  # k = 12: the 16-slot combine
 ])
 def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     say(f"grouped bf16 T={T} H={H} I={I} E={E} k={k}")
@@ -409,6 +410,7 @@ def test_grouped_bf16(m, T, H, I, E, k, skew, seed):
     (400, 512, 256, 8, 2, False, 4),     # 8-block tiles
     (64, 1280, 640, 64, 8, False, 5),    # decode kernel: 8-row segments, 10 / 5 chunks through its ring
     (48, 1024, 896, 32, 8, False, 6),    # decode kernel: 12-row segments, 8 / 7 chunks
+    (64, 256, 128, 32, 16, False, 7),    # k = 16 (the largest): the 16-slot combine
 ])
 def test_grouped_exact_bitexact(m, T, H, I, E, k, skew, seed):
     say(f"grouped exact T={T} H={H} I={I} E={E} k={k}")
