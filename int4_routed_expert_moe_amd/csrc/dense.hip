@@ -15,7 +15,8 @@
 // straight from global memory (16 bytes per lane) into a register ring.
 // Decode-shaped problems (few rows) split K over the grid and write fp32
 // partials that a second kernel sums in a fixed order (deterministic), then
-// applies the epilogue.
+// applies the epilogue.  From 256 rows the 32x32x16 shape takes over, on tiles
+// of 128, 192 or 256 rows (k_dense32, k_dense32_dma below).
 #include <utility>
 
 #include "moe_common.h"
