@@ -70,6 +70,9 @@ def parse():
                     help="no run: summarise rocprofv3 --pmc folders (one per counter pass) of one workload into "
                          "profiles/moe_layer_<workload>_counters.md (per-dispatch means and derived rates)")
     ap.add_argument("--kernel-regex", default="k_grouped", help="kernels kept by --counters-from")
+    ap.add_argument("--counters-name", default="grouped",
+                    help="which kernels --counters-from summarises, for the title and the file name "
+                         "(other than 'grouped': profiles/moe_layer_<workload>_<name>_counters.md)")
     return ap.parse_args()
 
 
@@ -414,11 +417,12 @@ def counters_summary(args, cfg):
                 v = vals.setdefault(name, {}).setdefault(r["Counter_Name"], {})
                 v[key] = v.get(key, 0.0) + float(r["Counter_Value"])
     # kernel durations of the counted runs: the bench lines in each folder's log, if kept beside it
-    out = [f"# Counters of the grouped kernels, workload {cfg['name']}", "",
+    out = [f"# Counters of the {args.counters_name} kernels, workload {cfg['name']}", "",
            "Commands (on the MI355X, from the repository root; one counter pass each), then the summary:", "", "```"]
     out += list(args.profile_cmd or ["(not given)"])
     out += [f"python3 bench.py --workload {cfg['id']} --counters-from {' '.join(args.counters_from)}"
-            f" --kernel-regex '{args.kernel_regex}'", "```", "",
+            f" --kernel-regex '{args.kernel_regex}'"
+            + (f" --counters-name {args.counters_name}" if args.counters_name != "grouped" else ""), "```", "",
             "Per-dispatch means over every dispatch of the kernel in the run. Derived rates, with the "
             f"normalisations used: per-SIMD busy cycles = SQ_BUSY_CYCLES / {SQ_INSTANCES} (the counter sums its "
             f"{SQ_INSTANCES} shader-engine instances); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / {SIMDS} SIMDs / "
@@ -451,7 +455,8 @@ def counters_summary(args, cfg):
                              f"{kms[call]:.3f} ms, the {call} event time of the --bench-json run)")
             out += ["", f"Per-SIMD busy cycles per dispatch: {busy:.4g}. " + "; ".join(rates) + "."]
         out.append("")
-    path = os.path.join(ROOT, "profiles", f"moe_layer_{cfg['name']}_counters.md")
+    tag = "" if args.counters_name == "grouped" else f"_{args.counters_name}"
+    path = os.path.join(ROOT, "profiles", f"moe_layer_{cfg['name']}{tag}_counters.md")
     with open(path, "w") as f:
         f.write("\n".join(out))
     print(f"wrote {path}")
