@@ -341,10 +341,10 @@ def _routing(g, T, E, k, skew=False):
     (280, 256, 128, 8, 2, False, 4),     # 6-block tiles
     (400, 512, 256, 8, 2, True, 5),      # 8-block tiles, skewed
     (700, 256, 128, 6, 2, False, 6),     # 32x32 tiles over 2 K chunks (gate/up) and 1 (down)
-    # several column chunks per staged item, the load ring running across them:
-    (700, 1024, 512, 6, 2, False, 7),    # gate/up 8 K chunks, 2 per item; down 4 K chunks, 4 per item
-    (500, 1536, 384, 5, 2, True, 8),     # gate/up 1 per item; down 3 K chunks (the least), 2 per item
-    (700, 1280, 512, 6, 2, False, 9),    # gate/up 10 K chunks, 2 per item; down 1 per item
+    # K chunk counts against the staged 32x32 kernel's three-chunk loop and its tails:
+    (700, 1024, 512, 6, 2, False, 7),    # gate/up over 8 K chunks, down over 4
+    (500, 1536, 384, 5, 2, True, 8),     # gate/up over 12 K chunks, down over 3 (skewed)
+    (700, 1280, 512, 6, 2, False, 9),    # gate/up over 10 K chunks, down over 4
     (200, 512, 256, 8, 2, False, 10),    # mid-size segments (about 50 rows): tiles of 3 row blocks, split segments
     (150, 768, 384, 6, 2, True, 11),     # the same, skewed (one long segment, empty experts)
     (100, 256, 128, 32, 12, False, 12),  # k = 12: the 16-slot combine
