@@ -53,6 +53,7 @@ def parse():
                          "report it under 'prefill' (default: on for the default decode workload)")
     ap.add_argument("--no-prefill-leg", dest="prefill_leg", action="store_false")
     ap.add_argument("--no-hbm-probe", action="store_true", help="skip the streaming read and copy probes")
+    ap.add_argument("--no-mfma-probe", action="store_true", help="skip the matrix-core rate probe")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the forward recorded as a HIP graph (MoELayer.capture) instead of "
                          "eager forwards; the per-call times still come from eager forwards")
@@ -291,6 +292,40 @@ def hbm_probe():
     return {"read_GBs": best_read, "copy_rw_GBs": best_copy, "read_bytes": n, "copy_bytes": m,
             "read_frac_of_peak": best_read / HBM_PEAK_GBS,
             "method": "best of 5: 16-byte grid-strided loads over 4 GiB (4096 workgroups); torch copy of 2 GiB"}
+
+
+def mfma_probe():
+    """Context figure for the nominal matrix-core peak: independent accumulation
+    chains on register operands of the 32x32x16 bf16 shape (the dense and prefill
+    kernels', 8 chains per wave) and of the 16x16x32 f16 shape (the 16x16 tile and
+    decode kernels', 16 chains per wave), two waves per SIMD (512 workgroups of 4
+    waves), best of 3."""
+    import ctypes
+
+    import torch
+    from int4_routed_expert_moe_amd import build as _b
+    lib = ctypes.CDLL(_b.PROBE_OUT)
+    lib.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.moe_probe_mfma.restype = ctypes.c_int
+    blocks, iters = 512, 10000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for shape, key, flops_per, chains in ((0, "bf16_32x32x16_TFs", 32768, 8), (1, "f16_16x16x32_TFs", 16384, 16)):
+        best = 0.0
+        for _ in range(4):  # the first run warms up
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            if lib.moe_probe_mfma(shape, ctypes.c_void_p(out.data_ptr()), blocks, iters, st) != 0:
+                raise RuntimeError("matrix-core probe launch failed")
+            b.record()
+            torch.cuda.synchronize()
+            best = max(best, blocks * 4 * chains * iters * flops_per / (a.elapsed_time(b) / 1e3) / 1e12)
+        res[key] = best
+    res["frac_of_peak"] = max(res["bf16_32x32x16_TFs"], res["f16_16x16x32_TFs"]) / MFMA_F16_PEAK_TFS
+    res["method"] = ("best of 3: independent chains on register operands (8 per wave for 32x32x16, 16 for "
+                     "16x16x32), 512 workgroups of 4 waves (two waves per SIMD), 10000 rounds")
+    return res
 
 
 def gemm_reference():
@@ -578,6 +613,8 @@ def main():
 
     if not args.no_hbm_probe:
         line["hbm_probe"] = hbm_probe()
+    if not args.no_mfma_probe:
+        line["mfma_probe"] = mfma_probe()
     if args.gemm_reference:
         line["gemm_reference"] = gemm_reference()
 

@@ -17,8 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe_int4.so")
-# the benchmark's HBM read probe: its own library, outside the layer's C ABI
-PROBE_SOURCES = ["hbm_probe.hip"]
+# the benchmark's HBM read and matrix-core rate probes: their own library, outside the layer's C ABI
+PROBE_SOURCES = ["hbm_probe.hip", "mfma_probe.hip"]
 PROBE_OUT = os.path.join(HERE, "libmoe_probe.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
